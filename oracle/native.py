@@ -1,0 +1,120 @@
+"""ctypes wrapper for the plain C part of the oracle (``ul_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: used by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+The C library holds the scalar index-loop relayout (sequence-sharded to
+head-sharded and back, "How Does Ulysses Sequence Parallelism Actually Work?",
+"Ulysses Sequence Parallelism: Training with Million-Token Contexts") and a
+scalar brute-force attention used to cross-check the float64 matrix oracle at
+tiny sizes.  It is built with gcc, ``-O2 -fopenmp``, no fast-math.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "ul_oracle.c"
+_LIB = _HERE / "libuloracle.so"
+
+_DT = {"f32": 0, "bf16": 1, "f64": 2}
+_lib = None
+
+
+def build(force: bool = True) -> Path:
+    """Compile ul_oracle.c into libuloracle.so next to it."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp")
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Werror",
+               "-o", str(tmp), str(_SRC), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+            build(force=True)
+        L = ctypes.CDLL(str(_LIB))
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+        L.oracle_attn_fwd_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
+                                           ctypes.c_int, vp, i64, vp, vp]
+        L.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
+                                      ctypes.c_int, vp, vp, vp]
+        for name in ("oracle_relayout_s2h", "oracle_relayout_h2s"):
+            getattr(L, name).argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
+        for f in (L.oracle_attn_fwd_rows, L.oracle_attn_bwd, L.oracle_relayout_s2h,
+                  L.oracle_relayout_h2s):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def relayout_s2h(x: np.ndarray, P: int) -> np.ndarray:
+    """[C, N, H, d] -> [C, P, N, H/P, d], element by element (any dtype)."""
+    x = np.ascontiguousarray(x)
+    C, N, H, d = x.shape
+    if P < 1 or H % P or N % P:
+        raise ValueError("need P >= 1, H % P == 0 and N % P == 0")
+    out = np.empty((C, P, N, H // P, d), dtype=x.dtype)
+    rc = lib().oracle_relayout_s2h(_ptr(x), _ptr(out), C, N, H, d, P, x.itemsize)
+    if rc:
+        raise RuntimeError(f"oracle_relayout_s2h failed ({rc})")
+    return out
+
+
+def relayout_h2s(y: np.ndarray) -> np.ndarray:
+    """[C, P, N, H/P, d] -> [C, N, H, d], element by element (any dtype)."""
+    y = np.ascontiguousarray(y)
+    C, P, N, Hs, d = y.shape
+    out = np.empty((C, N, Hs * P, d), dtype=y.dtype)
+    rc = lib().oracle_relayout_h2s(_ptr(y), _ptr(out), C, N, Hs * P, d, P, y.itemsize)
+    if rc:
+        raise RuntimeError(f"oracle_relayout_h2s failed ({rc})")
+    return out
+
+
+def _stored(x: np.ndarray, dtype: str) -> np.ndarray:
+    want = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}[dtype]
+    return np.ascontiguousarray(x, dtype=want)
+
+
+def brute_fwd(q, k, v, dtype: str, scale: float, causal: bool = True):
+    """Scalar brute-force forward: (o [B,N,Hq,d], lse [B,Hq,N]) in float64."""
+    q, k, v = (_stored(a, dtype) for a in (q, k, v))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    o = np.empty((B, N, Hq, d))
+    lse = np.empty((B, Hq, N))
+    rc = lib().oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, N, Hq, Hkv, d,
+                                    scale, int(causal), None, 0, _ptr(o), _ptr(lse))
+    if rc:
+        raise RuntimeError(f"oracle_attn_fwd_rows failed ({rc})")
+    return o, lse
+
+
+def brute_bwd(q, k, v, dout, dtype: str, scale: float, causal: bool = True):
+    """Scalar brute-force backward: (dq, dk, dv) in float64."""
+    q, k, v, dout = (_stored(a, dtype) for a in (q, k, v, dout))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    dq = np.empty((B, N, Hq, d))
+    dk = np.empty((B, N, Hkv, d))
+    dv = np.empty((B, N, Hkv, d))
+    rc = lib().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DT[dtype], B, N, Hq, Hkv,
+                               d, scale, int(causal), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc:
+        raise RuntimeError(f"oracle_attn_bwd failed ({rc})")
+    return dq, dk, dv
