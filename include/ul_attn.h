@@ -1,0 +1,162 @@
+/*
+ * ul_attn.h -- C ABI of libulattn.so: the per-rank hot path of Ulysses
+ * sequence parallelism on one MI355X (gfx950).
+ *
+ * The method ("Ulysses Sequence Parallelism: Training with Million-Token
+ * Contexts", section "How Does Ulysses Sequence Parallelism Actually Work?"):
+ * every GPU holds a chunk of N/P tokens; an all-to-all leaves each GPU with
+ * all N positions but only a slice of H/P heads; each GPU runs exact
+ * attention locally on its heads; a second all-to-all reverses the shuffle.
+ * This library provides the local pieces of that step:
+ *
+ *   ul_relayout_s2h   the sequence-sharded -> head-sharded permutation that the
+ *                     first all-to-all performs, done inside one GPU's memory;
+ *   ul_relayout_h2s   its inverse (the reversed shuffle);
+ *   ul_attn_fwd       causal (or full) softmax attention over the full N for a
+ *                     slice of query heads with grouped KV heads, also
+ *                     returning the per-row logsumexp;
+ *   ul_attn_bwd       its gradient (dQ, dK, dV).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  No call
+ *    allocates device memory, synchronises the device, or keeps state between
+ *    calls; every call validates its arguments on the host, enqueues its
+ *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
+ *    stream) and returns.  Results are ready when the stream reaches that
+ *    point.  Calls are thread-safe.
+ *  - All tensors are dense row-major (C order).
+ *  - Outputs are fully overwritten, never accumulated into.
+ *  - Errors are reported only through the returned status.  Validation runs
+ *    before any HIP call, so an invalid call enqueues nothing.
+ *    UL_ERR_HIP means a launch failed (hipGetLastError after the launch);
+ *    the output contents are then unspecified.
+ */
+#ifndef UL_ATTN_H
+#define UL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    UL_OK = 0,
+    UL_ERR_NULL = 1,         /* a required pointer is NULL */
+    UL_ERR_SHAPE = 2,        /* a size < 1, a non-finite or non-positive scale, or int64 overflow */
+    UL_ERR_DIVISIBILITY = 3, /* Hq % Hkv, H % P or N % P is non-zero, or P < 1 */
+    UL_ERR_UNSUPPORTED = 4,  /* head_dim or dtype outside what the kernels implement */
+    UL_ERR_ALIGNMENT = 5,    /* an attention tensor is not 16-byte aligned */
+    UL_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ul_attn_bwd_workspace_bytes */
+    UL_ERR_OVERLAP = 7,      /* an output's byte range overlaps an input or another output */
+    UL_ERR_HIP = 8           /* the HIP runtime reported an error at launch */
+} ul_status;
+
+typedef enum {
+    UL_F32 = 0,  /* IEEE binary32 inputs and outputs; fp32 arithmetic throughout */
+    UL_BF16 = 1  /* bfloat16 inputs and outputs; bf16 MFMA with fp32 accumulation */
+} ul_dtype;
+
+/*
+ * Forward attention for one rank's heads (section "How Does Ulysses Sequence
+ * Parallelism Actually Work?": attention over all N positions of a slice of
+ * heads, computed locally; "Ulysses: entrenar con contextos de hasta 96K
+ * tokens en 4 GPUs", section "Conclusion rapida": the attention mathematics
+ * itself is unchanged).
+ *
+ * For every batch b, query head h (KV head g = h / (Hq/Hkv), contiguous
+ * groups) and query row i:
+ *   s_ij   = softmax_scale * sum_e q[b,i,h,e] k[b,j,g,e]   for j <= i if causal
+ *                                                           (every j otherwise)
+ *   o[b,i,h,:] = sum_j softmax_j(s_ij) v[b,j,g,:]
+ *   lse[b,h,i] = ln sum_j exp(s_ij)                         (natural log)
+ *
+ *   q, o        [B][N][Hq][head_dim]   dtype
+ *   k, v        [B][N][Hkv][head_dim]  dtype
+ *   lse         [B][Hq][N]             fp32 (for either dtype)
+ *   head_dim    64 or 128
+ *   causal      1 = key j visible to query i iff j <= i; 0 = all keys visible
+ *   dtype       ul_dtype
+ * bf16 outputs are rounded to nearest-even from fp32 accumulators.
+ * Deterministic: identical inputs give bit-identical outputs.
+ * Errors: NULL, SHAPE, DIVISIBILITY (Hq % Hkv), UNSUPPORTED, ALIGNMENT,
+ * OVERLAP (o or lse overlapping q, k, v or each other), HIP.
+ */
+ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                      float softmax_scale, int32_t causal, int32_t dtype, void *stream);
+
+/*
+ * Device workspace bytes that ul_attn_bwd needs for these sizes (a multiple
+ * of 256).  Returns 0 for invalid sizes.
+ */
+size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t dtype);
+
+/*
+ * Backward of ul_attn_fwd: the gradient of L = <dout, o> with respect to q,
+ * k and v (training the method implies it; the pages give no formula, so it
+ * is the plain derivative of the forward above).  With
+ *   p_ij  = exp(s_ij - lse_i),  dp_ij = dout_i . v_j,  D_i = dout_i . o_i,
+ *   ds_ij = p_ij (dp_ij - D_i):
+ *   dq_i = softmax_scale * sum_j ds_ij k_j
+ *   dk_j = softmax_scale * sum over the group's query heads and rows i of ds_ij q_i
+ *   dv_j = sum over the group's query heads and rows i of p_ij dout_i
+ *
+ *   o, lse      outputs of ul_attn_fwd for the same q, k, v
+ *   dout, dq    [B][N][Hq][head_dim]   dtype
+ *   dk, dv      [B][N][Hkv][head_dim]  dtype
+ *   workspace   device buffer of at least ul_attn_bwd_workspace_bytes(...)
+ *               bytes, caller-owned, 16-byte aligned; its contents on entry
+ *               do not matter and are scratch afterwards.
+ * Deterministic: no atomics; identical inputs give bit-identical outputs.
+ * Errors: as ul_attn_fwd, plus WORKSPACE, and OVERLAP when dq, dk, dv or the
+ * workspace overlap each other or any input.
+ */
+ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                      void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
+                      int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                      int32_t dtype, void *stream);
+
+/*
+ * Sequence-sharded -> head-sharded relayout (the first all-to-all of the
+ * step, section "How Does Ulysses Sequence Parallelism Actually Work?": each
+ * GPU takes a chunk of N/P tokens, then ends up with all positions but a
+ * slice of heads), as one permutation in one GPU's memory:
+ *
+ *   in  [C][N][H][head_dim]       = [C][P][N/P][H][head_dim]: rank r's tokens
+ *                                   are the contiguous chunk [r*N/P, (r+1)*N/P)
+ *   out [C][P][N][H/P][head_dim]  rank r's contiguous head slice
+ *                                   [r*H/P, (r+1)*H/P) over all N tokens
+ *   out[c][r][t][hh][e] = in[c][t][r*(H/P) + hh][e]
+ *
+ * C is an outer batch (3 for a stacked Q/K/V tensor).  The copy moves bits:
+ * the result is byte-exact for any bit patterns.  H % P == 0 (which implies
+ * the method's rule that the head count be at least the parallel degree) and
+ * N % P == 0 (clean chunks, no padding) are required.  Any head_dim >= 1.
+ * Errors: NULL, SHAPE, DIVISIBILITY, UNSUPPORTED (dtype), OVERLAP (in and out
+ * byte ranges intersect: the permutation is not in place), HIP.
+ */
+ul_status ul_relayout_s2h(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                          int32_t head_dim, int32_t P, int32_t dtype, void *stream);
+
+/*
+ * Head-sharded -> sequence-sharded relayout (the reversed shuffle, and the
+ * adjoint of ul_relayout_s2h used on gradients):
+ *   in  [C][P][N][H/P][head_dim],  out [C][N][H][head_dim]
+ *   out[c][t][h][e] = in[c][h / (H/P)][t][h % (H/P)][e]
+ * Same requirements and errors as ul_relayout_s2h.
+ */
+ul_status ul_relayout_h2s(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                          int32_t head_dim, int32_t P, int32_t dtype, void *stream);
+
+/* Static, NUL-terminated name of a status code ("UL_OK", ...). */
+const char *ul_status_str(ul_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UL_ATTN_H */

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library builds, loads, exports every declared symbol, and its
+host-side validation returns the documented status codes before any HIP call.
+
+These calls pass fake (never dereferenced) device addresses and invalid arguments only, so
+no kernel is launched and no GPU is needed.
+"""
+
+import ctypes
+
+import pytest
+
+from ulysses_sequence_parallelism_attn_amd import binding as B
+from ulysses_sequence_parallelism_attn_amd import build as Bld
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not B.LIB_PATH.exists():
+        Bld.build()
+    return B.lib()
+
+
+A = 0x10000  # fake, 16-byte aligned addresses far apart
+BIG = 1 << 40
+
+
+def addr(i):
+    return ctypes.c_void_p(A + i * BIG)
+
+
+def test_exports_every_declared_symbol(L):
+    names = B.declared_functions()
+    assert set(names) == {"ul_attn_fwd", "ul_attn_bwd", "ul_attn_bwd_workspace_bytes",
+                          "ul_relayout_s2h", "ul_relayout_h2s", "ul_status_str"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code, name in B.STATUS.items():
+        assert L.ul_status_str(code).decode() == name
+    assert L.ul_status_str(99).decode() == "UL_ERR_UNKNOWN"
+
+
+def fwd(L, q=None, k=None, v=None, o=None, lse=None, Bsz=1, N=128, Hq=8, Hkv=2, d=128, scale=0.088,
+        causal=1, dtype=B.UL_BF16):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    o = addr(3) if o is None else o
+    lse = addr(4) if lse is None else lse
+    return L.ul_attn_fwd(q, k, v, o, lse, Bsz, N, Hq, Hkv, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=ctypes.c_void_p(0)), 1), (dict(lse=ctypes.c_void_p(0)), 1),
+    (dict(N=0), 2), (dict(Bsz=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(d=0), 2),
+    (dict(scale=0.0), 2), (dict(scale=-1.0), 2), (dict(scale=float("inf")), 2),
+    (dict(scale=float("nan")), 2), (dict(causal=2), 2),
+    (dict(Hq=6, Hkv=4), 3),
+    (dict(d=96), 4), (dict(d=256), 4), (dict(dtype=7), 4),
+    (dict(q=ctypes.c_void_p(A + 8)), 5), (dict(lse=ctypes.c_void_p(4 * BIG + A + 4)), 5),
+    (dict(o=ctypes.c_void_p(A + 64)), 7), (dict(lse=ctypes.c_void_p(A + BIG + 16)), 7),
+    (dict(lse=ctypes.c_void_p(3 * BIG + A + 1024)), 7),
+    (dict(N=1 << 40), 2),
+])
+def test_fwd_validation(L, kw, code):
+    assert fwd(L, **kw) == code
+
+
+def bwd(L, ws_bytes=None, ws=None, **kw):
+    p = dict(Bsz=1, N=256, Hq=8, Hkv=2, d=128, scale=0.088, causal=1, dtype=B.UL_BF16)
+    p.update(kw)
+    need = L.ul_attn_bwd_workspace_bytes(p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"], p["dtype"])
+    ptrs = [addr(i) for i in range(9)]
+    for i, n in enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"]):
+        if n in p:
+            ptrs[i] = p.pop(n)
+    ws = addr(9) if ws is None else ws
+    return L.ul_attn_bwd(*ptrs, ws, need if ws_bytes is None else ws_bytes, p["Bsz"], p["N"], p["Hq"],
+                         p["Hkv"], p["d"], p["scale"], p["causal"], p["dtype"], None)
+
+
+def test_workspace_bytes(L):
+    n = L.ul_attn_bwd_workspace_bytes(1, 65536, 8, 2, 128, B.UL_BF16)
+    assert n >= 2 * 8 * 65536 * 4 and n % 256 == 0
+    assert L.ul_attn_bwd_workspace_bytes(1, 0, 8, 2, 128, B.UL_BF16) == 0
+    assert L.ul_attn_bwd_workspace_bytes(1, 8, 6, 4, 128, B.UL_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=ctypes.c_void_p(0)), 1), (dict(dv=ctypes.c_void_p(0)), 1),
+    (dict(ws=ctypes.c_void_p(0)), 6), (dict(ws_bytes=16), 6),
+    (dict(N=-5), 2), (dict(Hq=3, Hkv=2), 3), (dict(d=80), 4),
+    (dict(dk=ctypes.c_void_p(A + 7 * BIG + 8)), 5),
+    (dict(dq=ctypes.c_void_p(A + 3 * BIG)), 7),   # dq aliases o
+    (dict(dk=ctypes.c_void_p(A + 8 * BIG)), 7),   # dk aliases dv
+    (dict(ws=ctypes.c_void_p(A + 6 * BIG + 256)), 7),  # workspace inside dq
+])
+def test_bwd_validation(L, kw, code):
+    assert bwd(L, **kw) == code
+
+
+@pytest.mark.parametrize("fn", ["ul_relayout_s2h", "ul_relayout_h2s"])
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 3, 64, 32, 128, 4, 1), 1),
+    ((A, A + BIG, 0, 64, 32, 128, 4, 1), 2),
+    ((A, A + BIG, 3, 64, 32, 0, 4, 1), 2),
+    ((A, A + BIG, 3, 64, 30, 128, 4, 1), 3),   # H % P
+    ((A, A + BIG, 3, 66, 32, 128, 4, 1), 3),   # N % P
+    ((A, A + BIG, 3, 64, 32, 128, 0, 1), 3),
+    ((A, A + BIG, 3, 64, 32, 128, 64, 1), 3),  # P > H: num_heads >= sp_size violated
+    ((A, A + BIG, 3, 64, 32, 128, 4, 5), 4),
+    ((A, A + 4096, 3, 64, 32, 128, 4, 1), 7),  # ranges overlap
+])
+def test_relayout_validation(L, fn, args, code):
+    a = [ctypes.c_void_p(args[0]), ctypes.c_void_p(args[1]), *args[2:], None]
+    assert getattr(L, fn)(*a) == code
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "LIB_PATH", tmp_path / "missing.so")
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

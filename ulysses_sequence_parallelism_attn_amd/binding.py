@@ -1,0 +1,171 @@
+"""Thin ctypes binding over libulattn.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module only turns
+torch tensors into device pointers and sizes, passes torch's current HIP
+stream, and raises :class:`UlError` on a non-zero status.  PyTorch provides
+device memory and streams, nothing else.  If the library has not been built,
+:func:`lib` raises instead of falling back to anything.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libulattn.so"
+HEADER = PKG.parent / "include" / "ul_attn.h"
+
+UL_F32, UL_BF16 = 0, 1
+STATUS = {0: "UL_OK", 1: "UL_ERR_NULL", 2: "UL_ERR_SHAPE", 3: "UL_ERR_DIVISIBILITY",
+          4: "UL_ERR_UNSUPPORTED", 5: "UL_ERR_ALIGNMENT", 6: "UL_ERR_WORKSPACE",
+          7: "UL_ERR_OVERLAP", 8: "UL_ERR_HIP"}
+
+_lib = None
+
+
+class UlError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{fn} failed: {self.name}")
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/ul_attn.h declares."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ul_\w+)\s*\(", text, re.M)))
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m ulysses_sequence_parallelism_attn_amd.build`"
+            )
+        L = ctypes.CDLL(str(LIB_PATH))
+        vp, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float,
+                                 ctypes.c_size_t)
+        L.ul_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32, i32, vp]
+        L.ul_attn_fwd.restype = ctypes.c_int
+        L.ul_attn_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+        L.ul_attn_bwd_workspace_bytes.restype = sz
+        L.ul_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32,
+                                  i32, f32, i32, i32, vp]
+        L.ul_attn_bwd.restype = ctypes.c_int
+        for name in ("ul_relayout_s2h", "ul_relayout_h2s"):
+            f = getattr(L, name)
+            f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
+            f.restype = ctypes.c_int
+        L.ul_status_str.argtypes = [ctypes.c_int]
+        L.ul_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise UlError(fn, st)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return UL_BF16
+    if t.dtype == torch.float32:
+        return UL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t, name: str):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None, lse=None,
+             stream=None):
+    """O, lse = attention(q, k, v).  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or fp32)."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().ul_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, N, Hq, Hkv, d,
+                           scale, int(causal), _dtype_code(q), _stream(stream))
+    _check("ul_attn_fwd", st)
+    return o, lse_t
+
+
+def workspace_bytes(B, N, Hq, Hkv, d, dtype_code) -> int:
+    return int(lib().ul_attn_bwd_workspace_bytes(B, N, Hq, Hkv, d, dtype_code))
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = True,
+             workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """dq, dk, dv of L = <dout, attention(q, k, v)>."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
+        _require(t, n)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    need = workspace_bytes(B, N, Hq, Hkv, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib().ul_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, N, Hq, Hkv,
+                           d, scale, int(causal), code, _stream(stream))
+    _check("ul_attn_bwd", st)
+    return dq, dk, dv
+
+
+def relayout_s2h(x, P: int, out=None, stream=None):
+    """[C, N, H, d] sequence-sharded world view -> [C, P, N, H/P, d] head-sharded."""
+    import torch
+
+    _require(x, "x")
+    C, N, H, d = x.shape
+    if P < 1 or H % P:
+        raise ValueError("H must be a multiple of P")
+    y = torch.empty((C, P, N, H // P, d), dtype=x.dtype, device=x.device) if out is None else out
+    st = lib().ul_relayout_s2h(_ptr(x), _ptr(y), C, N, H, d, P, _dtype_code(x), _stream(stream))
+    _check("ul_relayout_s2h", st)
+    return y
+
+
+def relayout_h2s(y, out=None, stream=None):
+    """[C, P, N, H/P, d] head-sharded -> [C, N, H, d] sequence-sharded."""
+    import torch
+
+    _require(y, "y")
+    C, P, N, Hs, d = y.shape
+    x = torch.empty((C, N, Hs * P, d), dtype=y.dtype, device=y.device) if out is None else out
+    st = lib().ul_relayout_h2s(_ptr(y), _ptr(x), C, N, Hs * P, d, P, _dtype_code(y),
+                               _stream(stream))
+    _check("ul_relayout_h2s", st)
+    return x

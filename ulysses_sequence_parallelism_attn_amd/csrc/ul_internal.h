@@ -1,0 +1,64 @@
+// ul_internal.h -- internal declarations shared by the host API and the HIP
+// kernel files of libulattn.so (not installed, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ul_attn.h"
+
+namespace ul {
+
+// Unsigned 32-bit division by a runtime-invariant divisor d >= 1 with one
+// multiply-high, an add and two shifts (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, unsigned case): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+//   t = mulhi(m, n),  n / d = (t + ((n - t) >> min(l,1))) >> max(l-1,0).
+struct FastDiv32 {
+    uint32_t d = 1, m = 1, sh1 = 0, sh2 = 0;
+    FastDiv32() = default;
+    explicit FastDiv32(uint32_t div) : d(div) {
+        uint32_t l = 0;
+        while ((1ull << l) < div) ++l;
+        m = (uint32_t)((((1ull << l) - div) << 32) / div + 1);
+        sh1 = l < 1 ? l : 1;
+        sh2 = l > 1 ? l - 1 : 0;
+    }
+    __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const uint32_t t = __umulhi(n, m);
+#else
+        const uint32_t t = (uint32_t)(((uint64_t)n * m) >> 32);
+#endif
+        return (t + ((n - t) >> sh1)) >> sh2;
+    }
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already
+// validated by the host API.
+
+hipError_t launch_relayout(const void *in, void *out, int64_t C, int64_t N, int64_t H, int64_t d,
+                           int64_t P, int64_t elt, bool to_head, hipStream_t stream);
+
+struct AttnShape {
+    int64_t B, N;
+    int32_t Hq, Hkv, d;
+    float scale;
+    int32_t causal;
+};
+
+hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
+                               float *lse, const AttnShape &s, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
+                                const AttnShape &s, hipStream_t stream);
+
+size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t dtype);
+hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
+                               const float *dout, const float *lse, float *dq, float *dk,
+                               float *dv, void *ws, const AttnShape &s, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
+                                const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                                void *ws, const AttnShape &s, hipStream_t stream);
+
+}  // namespace ul
