@@ -25,6 +25,8 @@
 // are rounded to bf16 for the MFMA.  fp32 kernels are plain VALU loops (the
 // exactness path).
 
+#include <type_traits>
+
 #include "mfma_tile.h"
 #include "ul_internal.h"
 
@@ -77,101 +79,96 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
 }
 
 // ============================================================================ bf16: dQ kernel
+//
+// Geometry as the forward: 8 waves (2 per SIMD), 32 query rows per wave; the
+// waves of a workgroup are the GQA group's query heads at the same positions,
+// so each K/V tile staged in LDS serves all of them.  Per 64-key tile and
+// 32-key half js:
+//   S^T  = K Q^T       (A = K rows, B = Q^T fragments in registers)
+//   dP^T = V dO^T      (A = V rows, B = dO^T fragments in registers)
+//   dS^T = P^T (dP^T - D),  P^T = exp2(S^T c - lse2)
+//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads, B = dS^T from C)
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 64;
+constexpr int kQWaves = 8;
+constexpr int kQThreads = kQWaves * 64;
+constexpr int kRowsPerWave = 32;
 constexpr int kKT = 64;
 
 struct DqParams {
     const uint16_t *q, *k, *v, *dout;
     const float *lse2, *Dv;
     uint16_t *dq;
-    int64_t N;
-    int32_t B, Hq, Hkv;
+    int32_t N, B, Hq, Hkv;
     int32_t heads_per_wg, pos_blocks, head_groups, n_qblk;
     float scale_log2, scale;
     int32_t causal;
 };
 
 template <int D>
-struct DqSmem {
-    u32x4 kt[2][kKT * D / 8];   // K rows (row-major, swizzled)
-    u32x4 vt[2][kKT * D / 8];   // V rows
-    u32x4 ktt[2][D * kKT / 8];  // K^T
+struct DqTile {
+    static constexpr int kBytes = kKT * D * 2;
+    static constexpr int kStage = 2 * kBytes;  // K then V
+    static constexpr int kLds = 2 * kStage;
 };
 
-template <int D>
-struct DqTileRegs {
-    static constexpr int kRowUnits = kKT * (D / 8) / (kWaves * 64);
-    static constexpr int kPairUnits = (kKT / 2) * (D / 8) / (kWaves * 64);
-    u32x4 k[kRowUnits], v[kRowUnits];
-    u32x4 t0[kPairUnits], t1[kPairUnits];
-};
-
-template <int D>
-__device__ __forceinline__ void load_rows(u32x4 *dst, const uint16_t *__restrict__ base,
-                                          int64_t row_stride, int64_t r0, int64_t N, int tid,
-                                          int units) {
-    constexpr int GPR = D / 8;
-    for (int u = 0; u < units; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int row = idx / GPR, gran = idx % GPR;
-        const int64_t r = r0 + row;
-        dst[u] = (r < N) ? *reinterpret_cast<const u32x4 *>(base + r * row_stride + gran * 8)
-                         : u32x4{0, 0, 0, 0};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void load_pairs(u32x4 *d0, u32x4 *d1, const uint16_t *__restrict__ base,
-                                           int64_t row_stride, int64_t r0, int64_t N, int tid,
-                                           int units) {
-    constexpr int GPR = D / 8;
-    for (int u = 0; u < units; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int kp = idx / GPR, gran = idx % GPR;
-        const int64_t r = r0 + 2 * kp;
-        d0[u] = (r < N) ? *reinterpret_cast<const u32x4 *>(base + r * row_stride + gran * 8)
-                        : u32x4{0, 0, 0, 0};
-        d1[u] = (r + 1 < N) ? *reinterpret_cast<const u32x4 *>(base + (r + 1) * row_stride + gran * 8)
-                            : u32x4{0, 0, 0, 0};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_rows(u32x4 *tile, const u32x4 *src, int tid, int units) {
-    constexpr int GPR = D / 8;
-    for (int u = 0; u < units; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        tile[rm_slot<D>(idx / GPR, idx % GPR)] = src[u];
-    }
-}
-
-// Transposed store: rows (2kp, 2kp+1) x d-granule -> 8 packed words of the
-// [D][64] transposed tile.
-template <int D>
-__device__ __forceinline__ void store_pairs_t(u32x4 *tile, const u32x4 *s0, const u32x4 *s1, int tid,
-                                              int units) {
-    constexpr int GPR = D / 8;
-    uint32_t *t32 = reinterpret_cast<uint32_t *>(tile);
-    for (int u = 0; u < units; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int kp = idx / GPR, gran = idx % GPR;
-        const int kgran = kp >> 2, within = kp & 3;
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_tile(f32x16 *dqacc, const bf16x8 *qf, const bf16x8 *dof,
+                                        float lse2, float Drow, const UL_LDS unsigned char *kt,
+                                        const UL_LDS unsigned char *vt, const TrAddr<D> &ta, int m,
+                                        int kg, int j0, int row, int N, int causal, float c) {
+    constexpr int KK = D / 16, EB = D / 32;
+    const int krow = kperm(m);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t a = s0[u][s >> 1], b = s1[u][s >> 1];
-            const uint32_t lo = (s & 1) ? (a >> 16) : (a & 0xffffu);
-            const uint32_t hi = (s & 1) ? (b & 0xffff0000u) : (b << 16);
-            t32[tr_slot<64>(gran * 8 + s, kgran) * 4 + within] = lo | hi;
+    for (int js = 0; js < 2; ++js) {
+        f32x16 s = zero16(), dp = zero16();
+        bf16x8 ak = row_frag<D>(kt, js * 32 + krow, kg), av = row_frag<D>(vt, js * 32 + krow, kg);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 nk = ak, nv = av;
+            if (kk + 1 < KK) {
+                nk = row_frag<D>(kt, js * 32 + krow, (kk + 1) * 2 + kg);
+                nv = row_frag<D>(vt, js * 32 + krow, (kk + 1) * 2 + kg);
+            }
+            s = mfma32x32x16(ak, qf[kk], s);
+            dp = mfma32x32x16(av, dof[kk], dp);
+            ak = nk;
+            av = nv;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float ds[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int r = hh * 8 + q;
+                float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+                if constexpr (MASK) {
+                    const int j = j0 + js * 32 + ckey(r, kg);
+                    if (j >= N || (causal && j > row)) pv = 0.f;
+                }
+                ds[q] = pv * (dp[r] - Drow);
+            }
+            dsf[hh] = pack8(ds);
+        }
+        bf16x8 a = tr_frag<D>(kt, ta, js * 32, 0);
+#pragma unroll
+        for (int st = 0; st < 2 * EB; ++st) {
+            const int hh = st / EB, eb = st % EB;
+            bf16x8 n = a;
+            if (st + 1 < 2 * EB) n = tr_frag<D>(kt, ta, js * 32 + ((st + 1) / EB) * 16, ((st + 1) % EB) * 32);
+            dqacc[eb] = mfma32x32x16(a, dsf[hh], dqacc[eb]);
+            a = n;
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_bwd_dq_bf16_kernel(DqParams p) {
+__global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    DqSmem<D> &sm = *reinterpret_cast<DqSmem<D> *>(smem_raw);
+    UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
+    using T = DqTile<D>;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
@@ -186,9 +183,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bwd_dq_bf16_kernel(DqPara
     const int qblk = p.causal ? (p.n_qblk - 1 - rank) : rank;
     const int grp = p.Hq / p.Hkv;
     const int h = g * grp + hg * p.heads_per_wg + (wave % p.heads_per_wg);
-    const int64_t wg_pos0 = (int64_t)qblk * kRowsPerWave * p.pos_blocks;
-    const int64_t i0 = wg_pos0 + (int64_t)(wave / p.heads_per_wg) * kRowsPerWave;
-    const int64_t N = p.N;
+    const int wg_rows = kRowsPerWave * p.pos_blocks;
+    const int wg_pos0 = qblk * wg_rows;
+    const int i0 = wg_pos0 + (wave / p.heads_per_wg) * kRowsPerWave;
+    const int N = p.N;
+    const int row = i0 + m;
     const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
     const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
     const uint16_t *dob = p.dout + ((int64_t)b * N * p.Hq + h) * D;
@@ -196,173 +195,209 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bwd_dq_bf16_kernel(DqPara
     const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
 
     constexpr int KK = D / 16, EB = D / 32;
-    bf16x8 qf[2][KK], dof[2][KK];
-    float lse2[2], Drow[2];
+    bf16x8 qf[KK], dof[KK];
+    const bool ok = row < N;
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const int64_t i = i0 + ib * 32 + m;
-        const bool ok = i < N;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            qf[ib][kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(qb + i * q_rs + kk * 16 + kg * 8)
-                                      : u32x4{0, 0, 0, 0});
-            dof[ib][kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + i * q_rs + kk * 16 + kg * 8)
-                                       : u32x4{0, 0, 0, 0});
-        }
-        const int64_t so = ((int64_t)b * p.Hq + h) * N + (ok ? i : 0);
-        lse2[ib] = ok ? p.lse2[so] : 0.f;
-        Drow[ib] = ok ? p.Dv[so] : 0.f;
+    for (int kk = 0; kk < KK; ++kk) {
+        qf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(qb + row * q_rs + kk * 16 + kg * 8)
+                              : u32x4{0, 0, 0, 0});
+        dof[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + row * q_rs + kk * 16 + kg * 8)
+                               : u32x4{0, 0, 0, 0});
     }
+    const int64_t so = ((int64_t)b * p.Hq + h) * N + (ok ? row : 0);
+    const float lse2 = ok ? p.lse2[so] : 0.f;
+    const float Drow = ok ? p.Dv[so] : 0.f;
 
-    f32x16 dqacc[EB][2];
+    f32x16 dqacc[EB];
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dqacc[eb][ib][r] = 0.f;
+    for (int eb = 0; eb < EB; ++eb) dqacc[eb] = zero16();
 
-    const int64_t wg_end = wg_pos0 + kRowsPerWave * p.pos_blocks;
-    const int64_t kend = p.causal ? (N < wg_end ? N : wg_end) : N;
-    const int ntiles = (int)((kend + kKT - 1) / kKT);
-    const int64_t wave_last_row = i0 + kRowsPerWave - 1;
+    const int kend = p.causal ? min(N, wg_pos0 + wg_rows) : N;
+    const int ntiles = (kend + kKT - 1) / kKT;
+    const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
+    const float c = p.scale_log2;
+    const TrAddr<D> ta(lane);
 
-    DqTileRegs<D> tr;
-    load_rows<D>(tr.k, kb, kv_rs, 0, N, tid, DqTileRegs<D>::kRowUnits);
-    load_rows<D>(tr.v, vb, kv_rs, 0, N, tid, DqTileRegs<D>::kRowUnits);
-    load_pairs<D>(tr.t0, tr.t1, kb, kv_rs, 0, N, tid, DqTileRegs<D>::kPairUnits);
-    store_rows<D>(sm.kt[0], tr.k, tid, DqTileRegs<D>::kRowUnits);
-    store_rows<D>(sm.vt[0], tr.v, tid, DqTileRegs<D>::kRowUnits);
-    store_pairs_t<D>(sm.ktt[0], tr.t0, tr.t1, tid, DqTileRegs<D>::kPairUnits);
+    TileStage<D, kKT, kQThreads> sk, sv;
+    sk.load(kb, kv_rs, 0, N, tid);
+    sv.load(vb, kv_rs, 0, N, tid);
+    sk.store(lds, tid);
+    sv.store(lds + T::kBytes, tid);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int st = t & 1;
-        const int64_t j0 = (int64_t)t * kKT;
+    auto step = [&](int t, auto masked, auto stage) {
+        constexpr int st = decltype(stage)::value;
+        const int j0 = t * kKT;
         if (t + 1 < ntiles) {
-            load_rows<D>(tr.k, kb, kv_rs, j0 + kKT, N, tid, DqTileRegs<D>::kRowUnits);
-            load_rows<D>(tr.v, vb, kv_rs, j0 + kKT, N, tid, DqTileRegs<D>::kRowUnits);
-            load_pairs<D>(tr.t0, tr.t1, kb, kv_rs, j0 + kKT, N, tid, DqTileRegs<D>::kPairUnits);
+            sk.load(kb, kv_rs, j0 + kKT, N, tid);
+            sv.load(vb, kv_rs, j0 + kKT, N, tid);
         }
-        const bool active = !p.causal || j0 <= wave_last_row;
-        if (active) {
-            const bool need_mask = (p.causal && j0 + kKT - 1 > i0) || j0 + kKT > N;
-#pragma unroll
-            for (int js = 0; js < 2; ++js) {
-                f32x16 sacc[2], pacc[2];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) { sacc[ib][r] = 0.f; pacc[ib][r] = 0.f; }
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const int row = js * 32 + kperm(m);
-                    const bf16x8 ak = as_bf16x8(sm.kt[st][rm_slot<D>(row, kk * 2 + kg)]);
-                    const bf16x8 av = as_bf16x8(sm.vt[st][rm_slot<D>(row, kk * 2 + kg)]);
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) {
-                        sacc[ib] = mfma32x32x16(ak, qf[ib][kk], sacc[ib]);
-                        pacc[ib] = mfma32x32x16(av, dof[ib][kk], pacc[ib]);
-                    }
-                }
-                // dS^T = P^T (dP^T - D), P^T = exp2(S^T * c - lse2)
-                bf16x8 dsf[2][2];
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const int64_t i = i0 + ib * 32 + m;
-                    float ds[16];
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float pv = __builtin_amdgcn_exp2f(fmaf(sacc[ib][r], p.scale_log2, -lse2[ib]));
-                        if (need_mask) {
-                            const int64_t j = j0 + js * 32 + ckey(r, kg);
-                            if (j >= N || (p.causal && j > i)) pv = 0.f;
-                        }
-                        ds[r] = pv * (pacc[ib][r] - Drow[ib]);
-                    }
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        dsf[hh][ib] = pack8(ds[hh * 8 + 0], ds[hh * 8 + 1], ds[hh * 8 + 2], ds[hh * 8 + 3],
-                                            ds[hh * 8 + 4], ds[hh * 8 + 5], ds[hh * 8 + 6], ds[hh * 8 + 7]);
-                }
-                // dQ^T += K^T dS^T over this subtile's 32 keys (2 k-steps of 16)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                    for (int eb = 0; eb < EB; ++eb) {
-                        const bf16x8 a = as_bf16x8(sm.ktt[st][tr_slot<64>(eb * 32 + m, (js * 2 + hh) * 2 + kg)]);
-#pragma unroll
-                        for (int ib = 0; ib < 2; ++ib) dqacc[eb][ib] = mfma32x32x16(a, dsf[hh][ib], dqacc[eb][ib]);
-                    }
-                }
-            }
+        const UL_LDS unsigned char *kt = lds + st * T::kStage;
+        const UL_LDS unsigned char *vt = kt + T::kBytes;
+        if constexpr (decltype(masked)::value) {
+            if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
+                dq_tile<D, true>(dqacc, qf, dof, lse2, Drow, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+        } else {
+            dq_tile<D, false>(dqacc, qf, dof, lse2, Drow, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
         }
         if (t + 1 < ntiles) {
-            store_rows<D>(sm.kt[st ^ 1], tr.k, tid, DqTileRegs<D>::kRowUnits);
-            store_rows<D>(sm.vt[st ^ 1], tr.v, tid, DqTileRegs<D>::kRowUnits);
-            store_pairs_t<D>(sm.ktt[st ^ 1], tr.t0, tr.t1, tid, DqTileRegs<D>::kPairUnits);
+            UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;
+            sk.store(nk, tid);
+            sv.store(nk + T::kBytes, tid);
         }
         __syncthreads();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    int t = 0;
+    for (; t + 1 < n_full; t += 2) {
+        step(t, std::false_type{}, S0{});
+        step(t + 1, std::false_type{}, S1{});
     }
+    if (t < n_full) {
+        step(t, std::false_type{}, S0{});
+        ++t;
+        if (t < ntiles) step(t, std::true_type{}, S1{});
+        ++t;
+    }
+    for (; t + 1 < ntiles; t += 2) {
+        step(t, std::true_type{}, S0{});
+        step(t + 1, std::true_type{}, S1{});
+    }
+    if (t < ntiles) step(t, std::true_type{}, S0{});
 
-    // dQ = scale * dQ^T^T, rounded to bf16
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const int64_t i = i0 + ib * 32 + m;
-        if (i >= N) continue;
-        uint16_t *row = p.dq + ((int64_t)b * N + i) * q_rs + (int64_t)h * D;
+    // dQ = scale * (dQ^T)^T, rounded to bf16: lane column = query row, registers = head dim
+    if (ok) {
+        uint16_t *out = p.dq + ((int64_t)b * N + row) * q_rs + (int64_t)h * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 bf16x4 o4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) o4[s] = (__bf16)(dqacc[eb][ib][r4 * 4 + s] * p.scale);
-                *reinterpret_cast<u32x2 *>(row + eb * 32 + r4 * 8 + kg * 4) = __builtin_bit_cast(u32x2, o4);
+                for (int q = 0; q < 4; ++q) o4[q] = (__bf16)(dqacc[eb][r4 * 4 + q] * p.scale);
+                *reinterpret_cast<u32x2 *>(out + eb * 32 + r4 * 8 + kg * 4) = __builtin_bit_cast(u32x2, o4);
             }
     }
 }
 
 // ============================================================================ bf16: dK/dV kernel
+//
+// 4 waves (one per SIMD, the full register file each), 32 keys per wave, 128
+// keys per workgroup for one KV head; steps over 64-row query tiles of every
+// query head of the group, from the causal diagonal to N.  Per step:
+//   S  = Q K^T,  dP = dO V^T     (A = Q / dO rows from LDS, B = K / V fragments in registers)
+//   P = exp2(S c - lse2), dS = P (dP - D)   (lane column = key, registers = query rows)
+//   dV^T += dO^T P,  dK^T += Q^T dS         (A = dO^T / Q^T by transposed LDS reads)
+// dK and dV are summed over the group's query heads in registers.
 
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kKeysPerWave = 32;
-constexpr int kKeysPerWg = kWaves * kKeysPerWave;  // 128
-constexpr int kQT = 64;                            // query rows per step
+constexpr int kKeysPerWg = kKvWaves * kKeysPerWave;  // 128
+constexpr int kQT = 64;                              // query rows per step
 
 struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
     const float *lse2, *Dv;
     uint16_t *dk, *dv;
-    int64_t N;
-    int32_t B, Hq, Hkv;
+    int32_t N, B, Hq, Hkv;
     int32_t n_kblk;
     float scale_log2, scale;
     int32_t causal;
 };
 
 template <int D>
-struct DkvSmem {
-    u32x4 qt[2][kQT * D / 8];    // Q rows
-    u32x4 dot[2][kQT * D / 8];   // dO rows
-    u32x4 qtt[2][D * kQT / 8];   // Q^T
-    u32x4 dott[2][D * kQT / 8];  // dO^T
-    float lse2[2][kQT];
-    float Dv[2][kQT];
+struct DkvTile {
+    static constexpr int kKV = kKeysPerWg * D * 2;     // static K or V tile of the workgroup
+    static constexpr int kBytes = kQT * D * 2;          // one Q or dO tile
+    static constexpr int kStats = 2 * kQT * 4;          // lse2 then D, fp32
+    static constexpr int kStage = 2 * kBytes + kStats;  // Q, dO, stats
+    static constexpr int kStage0 = 2 * kKV;
+    static constexpr int kLds = kStage0 + 2 * kStage;
 };
 
-template <int D>
-struct DkvTileRegs {
-    static constexpr int kRowUnits = kQT * (D / 8) / (kWaves * 64);
-    static constexpr int kPairUnits = (kQT / 2) * (D / 8) / (kWaves * 64);
-    u32x4 q[kRowUnits], d[kRowUnits];
-    u32x4 q0[kPairUnits], q1[kPairUnits], d0[kPairUnits], d1[kPairUnits];
-    float st;  // lse2 (tid < 64) or D (64 <= tid < 128)
-};
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_step(f32x16 *dkacc, f32x16 *dvacc, const UL_LDS unsigned char *kt,
+                                          const UL_LDS unsigned char *vt, int wrow,
+                                          const UL_LDS unsigned char *qt,
+                                          const UL_LDS unsigned char *dot,
+                                          const UL_LDS float *lse2s, const UL_LDS float *Ds,
+                                          const TrAddr<D> &ta, int m, int kg, int r0, int key,
+                                          int N, int causal, float c) {
+    constexpr int KK = D / 16, EB = D / 32;
+    const int qrow = kperm(m);
+    bf16x8 pf[4], dsf[4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+        f32x16 s = zero16(), dp = zero16();
+        // A = Q / dO rows (kperm order), B = this wave's K / V rows (column = key)
+        bf16x8 aq = row_frag<D>(qt, ib * 32 + qrow, kg), ad = row_frag<D>(dot, ib * 32 + qrow, kg);
+        bf16x8 bk = row_frag<D>(kt, wrow, kg), bv = row_frag<D>(vt, wrow, kg);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 nq = aq, nd = ad, nk = bk, nv = bv;
+            if (kk + 1 < KK) {
+                const int g = (kk + 1) * 2 + kg;
+                nq = row_frag<D>(qt, ib * 32 + qrow, g);
+                nd = row_frag<D>(dot, ib * 32 + qrow, g);
+                nk = row_frag<D>(kt, wrow, g);
+                nv = row_frag<D>(vt, wrow, g);
+            }
+            s = mfma32x32x16(aq, bk, s);
+            dp = mfma32x32x16(ad, bv, dp);
+            aq = nq;
+            ad = nd;
+            bk = nk;
+            bv = nv;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // C register r of lane group kg holds query row ib*32 + ckey(r, kg):
+        // runs of 8 consecutive rows, so the row statistics load as float4s.
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int rb = ib * 32 + hh * 16 + kg * 8;
+            const f32x4 l0 = *reinterpret_cast<const UL_LDS f32x4 *>(lse2s + rb);
+            const f32x4 l1 = *reinterpret_cast<const UL_LDS f32x4 *>(lse2s + rb + 4);
+            const f32x4 d0 = *reinterpret_cast<const UL_LDS f32x4 *>(Ds + rb);
+            const f32x4 d1 = *reinterpret_cast<const UL_LDS f32x4 *>(Ds + rb + 4);
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int r = hh * 8 + q;
+                const float lz = q < 4 ? l0[q] : l1[q - 4];
+                const float dz = q < 4 ? d0[q] : d1[q - 4];
+                float pz = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
+                if constexpr (MASK) {
+                    const int i = r0 + rb + q;
+                    if (i >= N || key >= N || (causal && key > i)) pz = 0.f;
+                }
+                pv[q] = pz;
+                dsv[q] = pz * (dp[r] - dz);
+            }
+            pf[ib * 2 + hh] = pack8(pv);
+            dsf[ib * 2 + hh] = pack8(dsv);
+        }
+    }
+    // dV^T += dO^T P ; dK^T += Q^T dS   (k = query rows, 4 steps of 16)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+            const bf16x8 ado = tr_frag<D>(dot, ta, ks * 16, eb * 32);
+            const bf16x8 aq = tr_frag<D>(qt, ta, ks * 16, eb * 32);
+            dvacc[eb] = mfma32x32x16(ado, pf[ks], dvacc[eb]);
+            dkacc[eb] = mfma32x32x16(aq, dsf[ks], dkacc[eb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_bwd_dkdv_bf16_kernel(DkvParams p) {
+__global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParams p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    DkvSmem<D> &sm = *reinterpret_cast<DkvSmem<D> *>(smem_raw);
+    UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
+    using T = DkvTile<D>;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
@@ -373,165 +408,109 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bwd_dkdv_bf16_kernel(DkvP
     const int bg = blockIdx.x - kblk * per_rank;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
-    const int64_t N = p.N;
+    const int N = p.N;
     const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
-    const int64_t kb0 = (int64_t)kblk * kKeysPerWg;
-    const int64_t jw0 = kb0 + wave * kKeysPerWave;  // this wave's first key
+    const int kb0 = kblk * kKeysPerWg;
+    const int wrow = wave * kKeysPerWave + m;   // this lane's key row in the static tiles
+    const int jw0 = kb0 + wave * kKeysPerWave;  // this wave's first key
+    const int key = kb0 + wrow;                 // this lane's key (C column)
 
-    constexpr int KK = D / 16, EB = D / 32;
-    // K and V fragments of this wave's 32 keys: B operand (column = key, k = head dim)
-    bf16x8 kf[KK], vf[KK];
+    constexpr int EB = D / 32;
     {
-        const int64_t j = jw0 + m;
-        const bool ok = j < N;
-        const uint16_t *kr = p.k + (((int64_t)b * N + (ok ? j : 0)) * p.Hkv + g) * D;
-        const uint16_t *vr = p.v + (((int64_t)b * N + (ok ? j : 0)) * p.Hkv + g) * D;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(kr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
-            vf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(vr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
-        }
+        const uint16_t *kb = p.k + ((int64_t)b * N * p.Hkv + g) * D;
+        const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
+        TileStage<D, kKeysPerWg, kKvThreads> sk;
+        sk.load(kb, kv_rs, kb0, N, tid);
+        sk.store(lds, tid);
+        sk.load(vb, kv_rs, kb0, N, tid);
+        sk.store(lds + T::kKV, tid);
     }
+    const UL_LDS unsigned char *kt = lds, *vt = lds + T::kKV;
     f32x16 dkacc[EB], dvacc[EB];
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { dkacc[eb][r] = 0.f; dvacc[eb][r] = 0.f; }
+    for (int eb = 0; eb < EB; ++eb) {
+        dkacc[eb] = zero16();
+        dvacc[eb] = zero16();
+    }
 
-    // Steps: every query head of the group x query tiles from the diagonal.
-    const int64_t qt_first = p.causal ? kb0 / kQT : 0;
-    const int64_t nqt = (N + kQT - 1) / kQT;
-    const int64_t per_head = nqt - qt_first;
-    const int64_t nsteps = per_head * grp;
+    // Steps: every query head of the group x 64-row tiles from the diagonal.
+    // A step needs no mask when its rows all lie at or after the workgroup's
+    // last key and inside N.
+    const int qt_first = p.causal ? kb0 / kQT : 0;
+    const int nqt = (N + kQT - 1) / kQT;
+    const int per_head = nqt - qt_first;
+    const int nsteps = per_head * grp;
+    const float c = p.scale_log2;
+    const TrAddr<D> ta(lane);
 
-    auto step_rows = [&](int64_t s, int &h, int64_t &r0) {
-        h = g * grp + (int)(s / per_head);
-        r0 = (qt_first + s % per_head) * kQT;
-    };
-    auto load_step = [&](DkvTileRegs<D> &tr, int64_t s) {
-        int h;
-        int64_t r0;
-        step_rows(s, h, r0);
+    TileStage<D, kQT, kKvThreads> sq, sd;
+    float stat = 0.f;  // lse2 (tid < 64) or D (64 <= tid < 128) of one row
+    auto load_step = [&](int s) {
+        const int h = g * grp + s / per_head;
+        const int r0 = (qt_first + s % per_head) * kQT;
         const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
         const uint16_t *db = p.dout + ((int64_t)b * N * p.Hq + h) * D;
-        load_rows<D>(tr.q, qb, q_rs, r0, N, tid, DkvTileRegs<D>::kRowUnits);
-        load_rows<D>(tr.d, db, q_rs, r0, N, tid, DkvTileRegs<D>::kRowUnits);
-        load_pairs<D>(tr.q0, tr.q1, qb, q_rs, r0, N, tid, DkvTileRegs<D>::kPairUnits);
-        load_pairs<D>(tr.d0, tr.d1, db, q_rs, r0, N, tid, DkvTileRegs<D>::kPairUnits);
+        sq.load(qb, q_rs, r0, N, tid);
+        sd.load(db, q_rs, r0, N, tid);
         if (tid < 2 * kQT) {
-            const int64_t i = r0 + (tid & (kQT - 1));
+            const int i = r0 + (tid & (kQT - 1));
             const int64_t so = ((int64_t)b * p.Hq + h) * N + i;
-            tr.st = (i < N) ? ((tid < kQT) ? p.lse2[so] : p.Dv[so]) : 0.f;
+            stat = i < N ? ((tid < kQT) ? p.lse2[so] : p.Dv[so]) : 0.f;
         }
     };
-    auto store_step = [&](const DkvTileRegs<D> &tr, int stage) {
-        store_rows<D>(sm.qt[stage], tr.q, tid, DkvTileRegs<D>::kRowUnits);
-        store_rows<D>(sm.dot[stage], tr.d, tid, DkvTileRegs<D>::kRowUnits);
-        store_pairs_t<D>(sm.qtt[stage], tr.q0, tr.q1, tid, DkvTileRegs<D>::kPairUnits);
-        store_pairs_t<D>(sm.dott[stage], tr.d0, tr.d1, tid, DkvTileRegs<D>::kPairUnits);
-        if (tid < kQT) sm.lse2[stage][tid] = tr.st;
-        else if (tid < 2 * kQT) sm.Dv[stage][tid - kQT] = tr.st;
+    auto store_step = [&](UL_LDS unsigned char *base) {
+        sq.store(base, tid);
+        sd.store(base + T::kBytes, tid);
+        if (tid < 2 * kQT) reinterpret_cast<UL_LDS float *>(base + 2 * T::kBytes)[tid] = stat;
     };
 
-    DkvTileRegs<D> tr;
     if (nsteps > 0) {
-        load_step(tr, 0);
-        store_step(tr, 0);
+        load_step(0);
+        store_step(lds + T::kStage0);
     }
     __syncthreads();
 
-    for (int64_t s = 0; s < nsteps; ++s) {
-        const int st = (int)(s & 1);
-        int h_unused;
-        int64_t r0;
-        step_rows(s, h_unused, r0);
-        if (s + 1 < nsteps) load_step(tr, s + 1);
-
-        // this wave's keys [jw0, jw0+32) vs rows [r0, r0+64)
-        const bool active = (!p.causal || jw0 <= r0 + kQT - 1) && jw0 < N;
-        if (active) {
-            const bool need_mask = (p.causal && jw0 + kKeysPerWave - 1 > r0) || r0 + kQT > N ||
-                                   jw0 + kKeysPerWave > N;
-            f32x16 sacc[2], pacc[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) { sacc[ib][r] = 0.f; pacc[ib][r] = 0.f; }
-            // S = Q K^T, dP = dO V^T: A = rows (permuted by kperm), B = key fragments
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib) {
-                    const int row = ib * 32 + kperm(m);
-                    const bf16x8 aq = as_bf16x8(sm.qt[st][rm_slot<D>(row, kk * 2 + kg)]);
-                    const bf16x8 ad = as_bf16x8(sm.dot[st][rm_slot<D>(row, kk * 2 + kg)]);
-                    sacc[ib] = mfma32x32x16(aq, kf[kk], sacc[ib]);
-                    pacc[ib] = mfma32x32x16(ad, vf[kk], pacc[ib]);
-                }
-            }
-            // P = exp2(S c - lse2_i); dS = P (dP - D_i); lane column = key, registers = rows
-            const int64_t j = jw0 + m;
-            bf16x8 pf[2][2], dsf[2][2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int rbase = ib * 32 + hh * 16 + kg * 8;  // 8 consecutive rows
-                    const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&sm.lse2[st][rbase]);
-                    const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&sm.lse2[st][rbase + 4]);
-                    const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sm.Dv[st][rbase]);
-                    const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sm.Dv[st][rbase + 4]);
-                    float pv[8], dsv[8];
-#pragma unroll
-                    for (int s8 = 0; s8 < 8; ++s8) {
-                        const int r = hh * 8 + s8;
-                        const float lz = s8 < 4 ? l0[s8] : l1[s8 - 4];
-                        const float dz = s8 < 4 ? d0[s8] : d1[s8 - 4];
-                        float pz = __builtin_amdgcn_exp2f(fmaf(sacc[ib][r], p.scale_log2, -lz));
-                        if (need_mask) {
-                            const int64_t i = r0 + rbase + s8;
-                            if (i >= N || j >= N || (p.causal && j > i)) pz = 0.f;
-                        }
-                        pv[s8] = pz;
-                        dsv[s8] = pz * (pacc[ib][r] - dz);
-                    }
-                    pf[ib][hh] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-                    dsf[ib][hh] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-                }
-            }
-            // dV^T += dO^T P ; dK^T += Q^T dS   (k = query row, 4 steps of 16)
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int kgran = (ib * 2 + hh) * 2 + kg;
-#pragma unroll
-                    for (int eb = 0; eb < EB; ++eb) {
-                        const bf16x8 ado = as_bf16x8(sm.dott[st][tr_slot<64>(eb * 32 + m, kgran)]);
-                        const bf16x8 aq = as_bf16x8(sm.qtt[st][tr_slot<64>(eb * 32 + m, kgran)]);
-                        dvacc[eb] = mfma32x32x16(ado, pf[ib][hh], dvacc[eb]);
-                        dkacc[eb] = mfma32x32x16(aq, dsf[ib][hh], dkacc[eb]);
-                    }
-                }
+    auto step = [&](int s, auto stage) {
+        constexpr int st = decltype(stage)::value;
+        const int r0 = (qt_first + s % per_head) * kQT;
+        if (s + 1 < nsteps) load_step(s + 1);
+        const UL_LDS unsigned char *base = lds + T::kStage0 + st * T::kStage;
+        const UL_LDS unsigned char *qt = base, *dot = base + T::kBytes;
+        const UL_LDS float *lse2s = reinterpret_cast<const UL_LDS float *>(base + 2 * T::kBytes);
+        const UL_LDS float *Ds = lse2s + kQT;
+        const bool full = (!p.causal || r0 >= kb0 + kKeysPerWg) && r0 + kQT <= N && kb0 + kKeysPerWg <= N;
+        if (full) {
+            dkdv_step<D, false>(dkacc, dvacc, kt, vt, wrow, qt, dot, lse2s, Ds, ta, m, kg, r0, key, N,
+                                p.causal, c);
+        } else if ((!p.causal || jw0 <= r0 + kQT - 1) && jw0 < N) {
+            dkdv_step<D, true>(dkacc, dvacc, kt, vt, wrow, qt, dot, lse2s, Ds, ta, m, kg, r0, key, N,
+                               p.causal, c);
         }
-        if (s + 1 < nsteps) store_step(tr, st ^ 1);
+        if (s + 1 < nsteps) store_step(lds + T::kStage0 + (st ^ 1) * T::kStage);
         __syncthreads();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+        step(s, S0{});
+        step(s + 1, S1{});
     }
+    if (s < nsteps) step(s, S0{});
 
-    // write dK = scale * acc, dV = acc (bf16); lane column = key, registers = head-dim rows
-    const int64_t j = jw0 + m;
-    if (j < N) {
-        uint16_t *dkr = p.dk + (((int64_t)b * N + j) * p.Hkv + g) * D;
-        uint16_t *dvr = p.dv + (((int64_t)b * N + j) * p.Hkv + g) * D;
+    // dK = scale * acc, dV = acc (bf16); lane column = key, registers = head dim
+    if (key < N) {
+        uint16_t *dkr = p.dk + (((int64_t)b * N + key) * p.Hkv + g) * D;
+        uint16_t *dvr = p.dv + (((int64_t)b * N + key) * p.Hkv + g) * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 bf16x4 k4, v4;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    k4[s] = (__bf16)(dkacc[eb][r4 * 4 + s] * p.scale);
-                    v4[s] = (__bf16)(dvacc[eb][r4 * 4 + s]);
+                for (int q = 0; q < 4; ++q) {
+                    k4[q] = (__bf16)(dkacc[eb][r4 * 4 + q] * p.scale);
+                    v4[q] = (__bf16)(dvacc[eb][r4 * 4 + q]);
                 }
                 const int e = eb * 32 + r4 * 8 + kg * 4;
                 *reinterpret_cast<u32x2 *>(dkr + e) = __builtin_bit_cast(u32x2, k4);
@@ -728,7 +707,6 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     hipError_t err = launch_pre(o, dout, lse, lse2, Dv, s, true, stream);
     if (err != hipSuccess) return err;
 
-    // dQ
     DqParams dp;
     dp.q = static_cast<const uint16_t *>(q);
     dp.k = static_cast<const uint16_t *>(k);
@@ -737,13 +715,13 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     dp.lse2 = lse2;
     dp.Dv = Dv;
     dp.dq = static_cast<uint16_t *>(dq);
-    dp.N = s.N;
+    dp.N = (int32_t)s.N;
     dp.B = (int32_t)s.B;
     dp.Hq = s.Hq;
     dp.Hkv = s.Hkv;
     const int grp = s.Hq / s.Hkv;
     dp.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
-    dp.pos_blocks = kWaves / dp.heads_per_wg;
+    dp.pos_blocks = kQWaves / dp.heads_per_wg;
     dp.head_groups = grp / dp.heads_per_wg;
     const int64_t pos_per_wg = (int64_t)kRowsPerWave * dp.pos_blocks;
     dp.n_qblk = (int32_t)((s.N + pos_per_wg - 1) / pos_per_wg);
@@ -762,7 +740,7 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     kp.Dv = Dv;
     kp.dk = static_cast<uint16_t *>(dk);
     kp.dv = static_cast<uint16_t *>(dv);
-    kp.N = s.N;
+    kp.N = (int32_t)s.N;
     kp.B = (int32_t)s.B;
     kp.Hq = s.Hq;
     kp.Hkv = s.Hkv;
@@ -774,21 +752,21 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     if (kv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
 
     if (s.d == 128) {
-        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<128>, sizeof(DqSmem<128>))) != hipSuccess) return err;
-        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<128>, sizeof(DkvSmem<128>))) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, dim3((uint32_t)dq_items), dim3(kWaves * 64),
-                           sizeof(DqSmem<128>), stream, dp);
+        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<128>, DqTile<128>::kLds)) != hipSuccess) return err;
+        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<128>, DkvTile<128>::kLds)) != hipSuccess) return err;
+        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, dim3((uint32_t)dq_items), dim3(kQThreads),
+                           DqTile<128>::kLds, stream, dp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, dim3((uint32_t)kv_items), dim3(kWaves * 64),
-                           sizeof(DkvSmem<128>), stream, kp);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, dim3((uint32_t)kv_items), dim3(kKvThreads),
+                           DkvTile<128>::kLds, stream, kp);
     } else {
-        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<64>, sizeof(DqSmem<64>))) != hipSuccess) return err;
-        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<64>, sizeof(DkvSmem<64>))) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, dim3((uint32_t)dq_items), dim3(kWaves * 64),
-                           sizeof(DqSmem<64>), stream, dp);
+        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<64>, DqTile<64>::kLds)) != hipSuccess) return err;
+        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<64>, DkvTile<64>::kLds)) != hipSuccess) return err;
+        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, dim3((uint32_t)dq_items), dim3(kQThreads),
+                           DqTile<64>::kLds, stream, dp);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, dim3((uint32_t)kv_items), dim3(kWaves * 64),
-                           sizeof(DkvSmem<64>), stream, kp);
+        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, dim3((uint32_t)kv_items), dim3(kKvThreads),
+                           DkvTile<64>::kLds, stream, kp);
     }
     return hipGetLastError();
 }

@@ -31,6 +31,8 @@
 // fp32 path: one thread per query row, K/V tiles in LDS, fp32 FMA and
 // online softmax; it is the exactness path (max-abs 1e-5), not a fast one.
 
+#include <type_traits>
+
 #include "mfma_tile.h"
 #include "ul_internal.h"
 
@@ -43,108 +45,139 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 // ============================================================================ bf16 MFMA kernel
 
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 64;
-constexpr int kKT = 64;  // keys per tile
+constexpr int kWaves = 8;                // 2 waves per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;         // query rows per wave (one MFMA column block)
+constexpr int kKT = 64;                  // keys per tile
 
 struct FwdParams {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
-    int64_t N;
-    int32_t B, Hq, Hkv;
-    int32_t heads_per_wg;   // query heads of one group handled by one workgroup (1, 2 or 4)
-    int32_t pos_blocks;     // 64-position blocks per workgroup = 4 / heads_per_wg
+    int32_t N, B, Hq, Hkv;
+    int32_t heads_per_wg;   // query heads of one KV group handled by one workgroup (1, 2 or 4)
+    int32_t pos_blocks;     // 32-position row blocks per workgroup = 8 / heads_per_wg
     int32_t head_groups;    // (Hq/Hkv) / heads_per_wg
-    int32_t n_qblk;         // ceil(N / (64 * pos_blocks))
+    int32_t n_qblk;         // ceil(N / (32 * pos_blocks))
     float scale_log2;       // softmax_scale * log2(e)
     int32_t causal;
 };
 
 template <int D>
-struct FwdSmem {
-    u32x4 kt[2][kKT * D / 8];  // K tile, row-major swizzled
-    u32x4 vt[2][D * kKT / 8];  // V^T tile, swizzled
+struct FwdTile {
+    static constexpr int kBytes = kKT * D * 2;  // one K or V tile
+    static constexpr int kStage = 2 * kBytes;   // K then V
+    static constexpr int kLds = 2 * kStage;     // double-buffered
 };
 
-// Stage one 64-key tile of K (row-major) and V (transposed) from registers.
+// Per-wave state carried across key tiles.
 template <int D>
-struct TileRegs {
-    static constexpr int kKUnits = kKT * (D / 8) / (kWaves * 64);       // 16-byte K granules per lane
-    static constexpr int kVUnits = (kKT / 2) * (D / 8) / (kWaves * 64); // (key pair, granule) per lane
-    u32x4 kg[kKUnits];
-    u32x4 v0[kVUnits], v1[kVUnits];
+struct FwdAcc {
+    static constexpr int EB = D / 32;
+    f32x16 o[EB];   // O^T: rows = head-dim, columns = this wave's 32 query rows
+    float m;        // running max of scaled scores, log2 units
+    float l;        // this lane's partial running sum (the other half holds the rest)
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D> &r, const uint16_t *__restrict__ kbase,
-                                          const uint16_t *__restrict__ vbase, int64_t row_stride,
-                                          int j0, int64_t N, int tid) {
-    constexpr int GPR = D / 8;  // granules per row
+// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+// MASK applies the causal diagonal and the ragged end of the sequence.
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
+                                         const UL_LDS unsigned char *kt,
+                                         const UL_LDS unsigned char *vt, const TrAddr<D> &ta,
+                                         int m, int kg, int j0, int row, int N, int causal,
+                                         float c) {
+    constexpr int KK = D / 16, EB = D / 32;
+    // S^T: one k-step of fragments in flight ahead of the MFMAs that use them
+    // (the barrier stops the scheduler from hoisting every LDS read of the
+    // tile, which would not fit in the register budget of 2 waves per SIMD).
+    f32x16 s[2] = {zero16(), zero16()};
+    const int krow = kperm(m);
+    bf16x8 a0 = row_frag<D>(kt, krow, kg), a1 = row_frag<D>(kt, 32 + krow, kg);
 #pragma unroll
-    for (int u = 0; u < TileRegs<D>::kKUnits; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int row = idx / GPR, gran = idx % GPR;
-        const int64_t j = j0 + row;
-        r.kg[u] = (j < N) ? *reinterpret_cast<const u32x4 *>(kbase + j * row_stride + gran * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < TileRegs<D>::kVUnits; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int kp = idx / GPR, gran = idx % GPR;
-        const int64_t j = j0 + 2 * kp;
-        r.v0[u] = (j < N) ? *reinterpret_cast<const u32x4 *>(vbase + j * row_stride + gran * 8)
-                          : u32x4{0, 0, 0, 0};
-        r.v1[u] = (j + 1 < N)
-                      ? *reinterpret_cast<const u32x4 *>(vbase + (j + 1) * row_stride + gran * 8)
-                      : u32x4{0, 0, 0, 0};
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D> &r, u32x4 *kt, u32x4 *vt, int tid) {
-    constexpr int GPR = D / 8;
-#pragma unroll
-    for (int u = 0; u < TileRegs<D>::kKUnits; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int row = idx / GPR, gran = idx % GPR;
-        kt[rm_slot<D>(row, gran)] = r.kg[u];
-    }
-    // V^T: the lane holds keys (2kp, 2kp+1) x d-values (8*gran .. 8*gran+7);
-    // it writes 8 packed key pairs, one 32-bit word per d row e.
-    uint32_t *vt32 = reinterpret_cast<uint32_t *>(vt);
-#pragma unroll
-    for (int u = 0; u < TileRegs<D>::kVUnits; ++u) {
-        const int idx = tid + u * kWaves * 64;
-        const int kp = idx / GPR, gran = idx % GPR;
-        const int kgran = kp >> 2, within = kp & 3;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint32_t a = r.v0[u][s >> 1], b = r.v1[u][s >> 1];
-            // element s of each row: low half for even s, high half for odd s
-            const uint32_t lo = (s & 1) ? (a >> 16) : (a & 0xffffu);
-            const uint32_t hi = (s & 1) ? (b & 0xffff0000u) : (b << 16);
-            const int e = gran * 8 + s;
-            vt32[tr_slot<kKT>(e, kgran) * 4 + within] = lo | hi;
+    for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (kk + 1 < KK) {
+            n0 = row_frag<D>(kt, krow, (kk + 1) * 2 + kg);
+            n1 = row_frag<D>(kt, 32 + krow, (kk + 1) * 2 + kg);
         }
+        s[0] = mfma32x32x16(a0, qf[kk], s[0]);
+        s[1] = mfma32x32x16(a1, qf[kk], s[1]);
+        a0 = n0;
+        a1 = n1;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (MASK) {
+                const int j = j0 + js * 32 + ckey(r, kg);
+                if (j >= N || (causal && j > row)) s[js][r] = -INFINITY;
+            }
+            mx = fmaxf(mx, s[js][r]);
+        }
+    const float tmax = half_max(mx) * c;
+
+    // Raise the running max only when the tile exceeds it by 2^8: O and l
+    // share the reference, so the result is exact either way.
+    const bool raise = tmax > acc.m + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float mnew = raise ? tmax : acc.m;
+        const float alpha = acc.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(acc.m - mnew);
+        acc.l *= alpha;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc.o[eb][r] *= alpha;
+        acc.m = mnew;
+    }
+
+    bf16x8 pf[4];
+    float ls = 0.f;
+#pragma unroll
+    for (int js = 0; js < 2; ++js)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                e[q] = __builtin_amdgcn_exp2f(fmaf(s[js][hh * 8 + q], c, -acc.m));
+                ls += e[q];
+            }
+            pf[js * 2 + hh] = pack8(e);
+        }
+    acc.l += ls;
+
+    // O^T += V^T P^T, same one-step lookahead
+    bf16x8 va = tr_frag<D>(vt, ta, 0, 0);
+#pragma unroll
+    for (int step = 0; step < 4 * EB; ++step) {
+        const int kap = step / EB, eb = step % EB;
+        bf16x8 vn = va;
+        if (step + 1 < 4 * EB) vn = tr_frag<D>(vt, ta, ((step + 1) / EB) * 16, ((step + 1) % EB) * 32);
+        acc.o[eb] = mfma32x32x16(va, pf[kap], acc.o[eb]);
+        va = vn;
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    FwdSmem<D> &sm = *reinterpret_cast<FwdSmem<D> *>(smem_raw);
+    UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
+    using T = FwdTile<D>;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
 
-    // ---- work item (longest first): item = rank * (B*Hkv*head_groups) + rest
+    // ---- work item, longest first: item = rank * (B*Hkv*head_groups) + rest
     const int per_rank = p.B * p.Hkv * p.head_groups;
-    const int item = blockIdx.x;
-    const int rank = item / per_rank;
-    int rest = item - rank * per_rank;
+    const int rank = blockIdx.x / per_rank;
+    int rest = blockIdx.x - rank * per_rank;
     const int g = rest % p.Hkv;
     rest /= p.Hkv;
     const int hg = rest % p.head_groups;
@@ -153,171 +186,105 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(FwdParams
 
     const int grp = p.Hq / p.Hkv;
     const int h = g * grp + hg * p.heads_per_wg + (wave % p.heads_per_wg);
-    const int64_t wg_pos0 = (int64_t)qblk * kRowsPerWave * p.pos_blocks;
-    const int64_t i0 = wg_pos0 + (int64_t)(wave / p.heads_per_wg) * kRowsPerWave;
-    const int64_t N = p.N;
+    const int wg_rows = kRowsPerWave * p.pos_blocks;
+    const int wg_pos0 = qblk * wg_rows;
+    const int i0 = wg_pos0 + (wave / p.heads_per_wg) * kRowsPerWave;
+    const int N = p.N;
+    const int row = i0 + m;
 
-    const int64_t q_rs = (int64_t)p.Hq * D;   // row stride of q / o
-    const int64_t kv_rs = (int64_t)p.Hkv * D; // row stride of k / v
+    const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
     const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
     const uint16_t *kb = p.k + ((int64_t)b * N * p.Hkv + g) * D;
     const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
 
-    // ---- Q^T fragments: B operand, column = query row, k = head dim
-    constexpr int KK = D / 16;
-    bf16x8 qf[2][KK];
+    // ---- Q^T fragments (B operand: column = query row, k = head dim)
+    constexpr int KK = D / 16, EB = D / 32;
+    bf16x8 qf[KK];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const int64_t i = i0 + ib * 32 + m;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qf[ib][kk] = as_bf16x8(i < N ? *reinterpret_cast<const u32x4 *>(qb + i * q_rs + kk * 16 + kg * 8)
-                                         : u32x4{0, 0, 0, 0});
-    }
+    for (int kk = 0; kk < KK; ++kk)
+        qf[kk] = as_bf16x8(row < N ? *reinterpret_cast<const u32x4 *>(qb + row * q_rs + kk * 16 + kg * 8)
+                                   : u32x4{0, 0, 0, 0});
 
-    constexpr int EB = D / 32;
-    f32x16 oacc[EB][2];
+    FwdAcc<D> acc;
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[eb][ib][r] = 0.f;
-    float mrow[2] = {-INFINITY, -INFINITY};
-    float lrow[2] = {0.f, 0.f};
+    for (int eb = 0; eb < EB; ++eb) acc.o[eb] = zero16();
+    acc.m = -INFINITY;
+    acc.l = 0.f;
 
-    const int64_t kend = p.causal ? (N < wg_pos0 + kRowsPerWave * p.pos_blocks ? N : wg_pos0 + kRowsPerWave * p.pos_blocks) : N;
-    const int ntiles = (int)((kend + kKT - 1) / kKT);
-    const int64_t wave_last_row = i0 + kRowsPerWave - 1;
+    // tiles [0, n_full) are visible to every row of the workgroup and inside N
+    const int kend = p.causal ? min(N, wg_pos0 + wg_rows) : N;
+    const int ntiles = (kend + kKT - 1) / kKT;
+    const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
+    const float c = p.scale_log2;
+    const TrAddr<D> ta(lane);
 
-    TileRegs<D> tr;
-    load_tile<D>(tr, kb, vb, kv_rs, 0, N, tid);
-    store_tile<D>(tr, sm.kt[0], sm.vt[0], tid);
+    TileStage<D, kKT, kThreads> sk, sv;
+    sk.load(kb, kv_rs, 0, N, tid);
+    sv.load(vb, kv_rs, 0, N, tid);
+    sk.store(lds, tid);
+    sv.store(lds + T::kBytes, tid);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int st = t & 1;
+    // One pipeline step: fetch tile t+1 into registers, compute tile t from
+    // LDS, park tile t+1 in the other LDS stage.  The unmasked and masked
+    // tiles run in separate loops so each loop keeps only its own invariants.
+    auto step = [&](int t, auto masked, auto stage) {
+        constexpr int st = decltype(stage)::value;
         const int j0 = t * kKT;
-        if (t + 1 < ntiles) load_tile<D>(tr, kb, vb, kv_rs, j0 + kKT, N, tid);
-
-        const bool active = !p.causal || (int64_t)j0 <= wave_last_row;
-        if (active) {
-            // ---- S^T = K Q^T for 2 key subtiles x 2 row blocks
-            f32x16 sacc[2][2];
-#pragma unroll
-            for (int js = 0; js < 2; ++js)
-#pragma unroll
-                for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sacc[js][ib][r] = 0.f;
-            const u32x4 *kt = sm.kt[st];
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-#pragma unroll
-                for (int js = 0; js < 2; ++js) {
-                    const bf16x8 a = as_bf16x8(kt[rm_slot<D>(js * 32 + kperm(m), kk * 2 + kg)]);
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) sacc[js][ib] = mfma32x32x16(a, qf[ib][kk], sacc[js][ib]);
-                }
-            }
-
-            // ---- mask (causal diagonal / ragged tail), scale to log2 units, row max
-            const bool need_mask = (p.causal && (int64_t)j0 + kKT - 1 > i0) || (int64_t)j0 + kKT > N;
-            float tmax[2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const int64_t i = i0 + ib * 32 + m;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int js = 0; js < 2; ++js)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float sv = sacc[js][ib][r] * p.scale_log2;
-                        if (need_mask) {
-                            const int64_t j = j0 + js * 32 + ckey(r, kg);
-                            if (j >= N || (p.causal && j > i)) sv = -INFINITY;
-                        }
-                        sacc[js][ib][r] = sv;
-                        mx = fmaxf(mx, sv);
-                    }
-                tmax[ib] = fmaxf(mx, __shfl_xor(mx, 32));
-            }
-
-            // ---- raise the running max only when a tile exceeds it by the slack
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                const bool raise = tmax[ib] > mrow[ib] + kRescaleSlack;
-                if (__any(raise)) {
-                    const float mnew = raise ? tmax[ib] : mrow[ib];
-                    const float alpha = (mrow[ib] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrow[ib] - mnew);
-                    lrow[ib] *= alpha;
-#pragma unroll
-                    for (int eb = 0; eb < EB; ++eb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[eb][ib][r] *= alpha;
-                    mrow[ib] = mnew;
-                }
-            }
-
-            // ---- P^T = exp2(S^T - m), row sums, bf16 fragments
-            bf16x8 pf[4][2];
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-                float ls = 0.f;
-#pragma unroll
-                for (int js = 0; js < 2; ++js)
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        float e[8];
-#pragma unroll
-                        for (int s = 0; s < 8; ++s) {
-                            e[s] = __builtin_amdgcn_exp2f(sacc[js][ib][hh * 8 + s] - mrow[ib]);
-                            ls += e[s];
-                        }
-                        pf[js * 2 + hh][ib] = pack8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-                    }
-                lrow[ib] += ls;
-            }
-
-            // ---- O^T += V^T P^T
-            const u32x4 *vt = sm.vt[st];
-#pragma unroll
-            for (int kap = 0; kap < 4; ++kap) {
-#pragma unroll
-                for (int eb = 0; eb < EB; ++eb) {
-                    const bf16x8 a = as_bf16x8(vt[tr_slot<kKT>(eb * 32 + m, kap * 2 + kg)]);
-#pragma unroll
-                    for (int ib = 0; ib < 2; ++ib) oacc[eb][ib] = mfma32x32x16(a, pf[kap][ib], oacc[eb][ib]);
-                }
-            }
+        if (t + 1 < ntiles) {
+            sk.load(kb, kv_rs, j0 + kKT, N, tid);
+            sv.load(vb, kv_rs, j0 + kKT, N, tid);
         }
-
-        if (t + 1 < ntiles) store_tile<D>(tr, sm.kt[st ^ 1], sm.vt[st ^ 1], tid);
+        const UL_LDS unsigned char *kt = lds + st * T::kStage;
+        const UL_LDS unsigned char *vt = kt + T::kBytes;
+        if constexpr (decltype(masked)::value) {
+            if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
+                fwd_tile<D, true>(acc, qf, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+        } else {
+            fwd_tile<D, false>(acc, qf, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+        }
+        if (t + 1 < ntiles) {
+            UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;
+            sk.store(nk, tid);
+            sv.store(nk + T::kBytes, tid);
+        }
         __syncthreads();
+    };
+    // Tiles go in pairs so that the LDS stage is a compile-time offset.
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    int t = 0;
+    for (; t + 1 < n_full; t += 2) {
+        step(t, std::false_type{}, S0{});
+        step(t + 1, std::false_type{}, S1{});
     }
+    if (t < n_full) {
+        step(t, std::false_type{}, S0{});
+        ++t;
+        if (t < ntiles) step(t, std::true_type{}, S1{});
+        ++t;
+    }
+    for (; t + 1 < ntiles; t += 2) {
+        step(t, std::true_type{}, S0{});
+        step(t + 1, std::true_type{}, S1{});
+    }
+    if (t < ntiles) step(t, std::true_type{}, S0{});
 
     // ---- epilogue: normalise, round to bf16, write O and lse
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        const float ltot = lrow[ib] + __shfl_xor(lrow[ib], 32);
+    const float ltot = half_sum(acc.l);
+    if (row < N) {
         const float inv = 1.f / ltot;
-        const int64_t i = i0 + ib * 32 + m;
-        if (i < N) {
-            uint16_t *orow = p.o + ((int64_t)b * N + i) * q_rs + (int64_t)h * D;
+        uint16_t *orow = p.o + ((int64_t)b * N + row) * q_rs + (int64_t)h * D;
 #pragma unroll
-            for (int eb = 0; eb < EB; ++eb)
+        for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) {
-                    const int e = eb * 32 + r4 * 8 + kg * 4;
-                    bf16x4 ov;
-                    ov[0] = (__bf16)(oacc[eb][ib][r4 * 4 + 0] * inv);
-                    ov[1] = (__bf16)(oacc[eb][ib][r4 * 4 + 1] * inv);
-                    ov[2] = (__bf16)(oacc[eb][ib][r4 * 4 + 2] * inv);
-                    ov[3] = (__bf16)(oacc[eb][ib][r4 * 4 + 3] * inv);
-                    *reinterpret_cast<u32x2 *>(orow + e) = __builtin_bit_cast(u32x2, ov);
-                }
-            if (kg == 0) p.lse[((int64_t)b * p.Hq + h) * N + i] = (mrow[ib] + log2f(ltot)) * kLn2;
-        }
+            for (int r4 = 0; r4 < 4; ++r4) {
+                bf16x4 ov;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ov[q] = (__bf16)(acc.o[eb][r4 * 4 + q] * inv);
+                *reinterpret_cast<u32x2 *>(orow + eb * 32 + r4 * 8 + kg * 4) = __builtin_bit_cast(u32x2, ov);
+            }
+        if (kg == 0) p.lse[((int64_t)b * p.Hq + h) * N + row] = (acc.m + __log2f(ltot)) * kLn2;
     }
 }
 
@@ -410,7 +377,7 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     p.v = static_cast<const uint16_t *>(v);
     p.o = static_cast<uint16_t *>(o);
     p.lse = lse;
-    p.N = s.N;
+    p.N = (int32_t)s.N;
     p.B = (int32_t)s.B;
     p.Hq = s.Hq;
     p.Hkv = s.Hkv;
@@ -425,12 +392,11 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     const int64_t items = (int64_t)p.n_qblk * p.B * p.Hkv * p.head_groups;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((uint32_t)items), block(kWaves * 64);
-    if (s.d == 128) {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, sizeof(FwdSmem<128>), stream, p);
-    } else {
-        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, sizeof(FwdSmem<64>), stream, p);
-    }
+    const dim3 grid((uint32_t)items), block(kThreads);
+    if (s.d == 128)
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, FwdTile<128>::kLds, stream, p);
+    else
+        hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, FwdTile<64>::kLds, stream, p);
     return hipGetLastError();
 }
 

@@ -1,20 +1,29 @@
-// mfma_tile.h -- gfx950 building blocks for the attention kernels: bf16
-// fragment types, the 32x32x16 bf16 MFMA, register/LDS layouts.
+// mfma_tile.h -- gfx950 building blocks shared by the attention kernels:
+// bf16 fragment types, the 32x32x16 bf16 MFMA, the register layouts of its
+// operands, and the swizzled LDS tile with row-major and transposed reads.
 //
 // Layout facts used throughout (v_mfma_f32_32x32x16_bf16, wave64):
-//  * A operand (32 x 16): lane l supplies row  (l % 32) and 8 k-values chosen
+//  * A operand (32 x 16): lane l supplies row (l % 32) and 8 k-values chosen
 //    by k-group kg = l / 32.
 //  * B operand (16 x 32): lane l supplies column (l % 32) and the same 8
 //    k-values of group kg.  Which 8 physical k's a slot holds is irrelevant as
-//    long as A and B agree, so every contraction below defines its own k order.
+//    long as A and B agree, so every contraction defines its own k order.
 //  * C/D (32 x 32 fp32, 16 regs): lane l holds column (l % 32); register r
 //    holds row 8*(r/4) + 4*(l/32) + (r%4).
 //
-// Key permutation: when a 32-key tile is the A operand of S^T = K Q^T, lane
-// row m loads key kperm(m) = 16*(m/16) + 8*((m/4)%2) + 4*((m/8)%2) + (m%4).
-// Then C register r of lane group kg holds key 16*(r/8) + 8*kg + (r%8): the 8
-// registers r = 8h..8h+7 hold 8 CONSECUTIVE keys, which is exactly a B-operand
-// fragment (k = key) for the next contraction over keys.
+// Row permutation: when a 32-row block is the A operand, lane row m loads
+// source row kperm(m) = 16*(m/16) + 8*((m/4)%2) + 4*((m/8)%2) + (m%4).  Then C
+// register r of lane group kg holds source row 16*(r/8) + 8*kg + (r%8): the 8
+// registers r = 8h..8h+7 hold 8 CONSECUTIVE source rows, which is exactly a
+// B-operand fragment (k = that row index) for the next contraction.
+//
+// LDS tiles are row-major [rows][D] bf16, addressed in 16-byte granules with
+// an XOR swizzle chosen so that both access patterns below are free of bank
+// conflicts on the 64 x 4-byte banks:
+//  * row reads (ds_read_b128): 16 lanes read granule g of 16 distinct rows
+//    that cover a full residue class mod 16;
+//  * transposed reads (ds_read_b64_tr_b16): 32 lanes read 4 granules of 4
+//    consecutive rows (4-aligned).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,36 +33,39 @@ namespace ul {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define UL_LDS __attribute__((address_space(3)))
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ u32x4 as_u32x4(const bf16x8 &b) { return __builtin_bit_cast(u32x4, b); }
 
-// Row (A-operand row / C row) m -> key offset within a 32-key tile.
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return z;
+}
+
+// A-operand lane row m -> source row within a 32-row block.
 __device__ __forceinline__ int kperm(int m) {
     return (m & 16) | ((m & 4) << 1) | ((m & 8) >> 1) | (m & 3);
 }
 
-// C register r of lane group kg in a 32x32 tile -> row index.
-__device__ __forceinline__ int crow(int r, int kg) { return ((r >> 2) << 3) | (kg << 2) | (r & 3); }
-
-// With kperm applied on the A side: C register r of lane group kg -> key.
+// With kperm applied on the A side: C register r of lane group kg -> source row.
 __device__ __forceinline__ int ckey(int r, int kg) { return ((r >> 3) << 4) | (kg << 3) | (r & 7); }
 
 // Eight fp32 values -> one bf16x8 fragment (round to nearest even).
-__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5,
-                                       float a6, float a7) {
+__device__ __forceinline__ bf16x8 pack8(const float *a) {
     bf16x8 r;
-    r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
-    r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) r[s] = (__bf16)a[s];
     return r;
 }
 
@@ -61,32 +73,106 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// ---------------------------------------------------------------------------
-// LDS tiles.  Both layouts are addressed in 16-byte granules with an XOR
-// swizzle so that the 16 lanes of a quarter-wave reading one granule column
-// hit 16 distinct granule slots of a 256-byte bank window.
-//
-// Row-major tile [rows][D] bf16 (K or V rows as A operands, Q/dO rows):
-//   granule G of row j lives at slot  j*(D/8) + (G ^ swz_rm(j)).
-template <int D>
-__device__ __forceinline__ int swz_rm(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+// Combine a value with the one held by the lane 32 positions away (both
+// halves of the wave get op(low, high)).  v_permlane32_swap exchanges the
+// halves of two registers; fed the same value twice, its two results hold
+// the low-half and the high-half value in every lane.
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-template <int D>
-__device__ __forceinline__ int rm_slot(int row, int gran) {
-    return row * (D / 8) + (gran ^ swz_rm<D>(row));
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Transposed tile [D][KT] bf16 (V^T or K^T, KT keys per row, 16 <= KT*2/16):
-// key granule KG (8 keys) of row e lives at slot  e*(KT/8) + (KG ^ swz_tr(e)).
-template <int KT>
-__device__ __forceinline__ int swz_tr(int e) {
-    // KT = 64: 8 granules per 128-byte row, two rows per 256-byte window.
-    return ((e >> 1) + (e >> 4)) & 7;
+// ---------------------------------------------------------------- LDS tiles
+
+// XOR applied to the granule index of row r (D = 128: 16 granules per
+// 256-byte row; D = 64: 8 granules per 128-byte row, two rows per bank window).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
-template <int KT>
-__device__ __forceinline__ int tr_slot(int e, int kgran) {
-    return e * (KT / 8) + (kgran ^ swz_tr<KT>(e));
+
+// Byte offset of granule g of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int g) {
+    return r * (D * 2) + ((g ^ swz<D>(r)) << 4);
 }
+
+// A/B fragment from a row: 8 consecutive elements starting at granule g of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const UL_LDS unsigned char *tile, int r, int g) {
+    const u32x4 v = *reinterpret_cast<const UL_LDS u32x4 *>(tile + tile_off<D>(r, g));
+    return as_bf16x8(v);
+}
+
+typedef __bf16 v4bf16 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+
+// Transposed A-operand fragment: element s of lane l is
+//   tile[r0 + 8*(l/32) + s][c0 + (l % 32)]       (s = 0..7)
+// for r0 a multiple of 8 and c0 a multiple of 32.  Two ds_read_b64_tr_b16:
+// within each 16-lane group, lane i receives element i%4 of the 4-element
+// chunks addressed by lanes 4k + i/4 (k = 0..3), so lane j of the group
+// addresses row 4*half + j/4 and columns 16*((l/16)%2) + 4*(j%4) .. +3.
+template <int D>
+struct TrAddr {
+    int row_off;  // 8*kg + j/4
+    int col_off;  // 16*((l/16)%2) + 4*(j%4)
+    __device__ __forceinline__ explicit TrAddr(int lane) {
+        const int j = lane & 15;
+        row_off = ((lane >> 5) << 3) + (j >> 2);
+        col_off = (((lane >> 4) & 1) << 4) + ((j & 3) << 2);
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const UL_LDS unsigned char *tile, const TrAddr<D> &ta, int r0,
+                                          int c0) {
+    const int c = c0 + ta.col_off;
+    const int g = c >> 3, within = (c & 7) << 1;
+    const int ra = r0 + ta.row_off, rb = ra + 4;
+    const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (UL_LDS v4bf16 *)(tile + tile_off<D>(ra, g) + within));
+    const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (UL_LDS v4bf16 *)(tile + tile_off<D>(rb, g) + within));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Cooperative tile staging: NT threads move ROWS x D bf16 between global
+// memory (row stride `stride` elements) and a swizzled LDS tile, 16 bytes per
+// lane per unit, consecutive lanes on consecutive granules of a row.
+template <int D, int ROWS, int NT>
+struct TileStage {
+    static constexpr int GPR = D / 8;                 // granules per row
+    static constexpr int UNITS = ROWS * GPR / NT;     // granules per thread
+    static_assert(ROWS * GPR % NT == 0, "tile must divide evenly among threads");
+    u32x4 v[UNITS];
+
+    // rows r0 + row >= nrows read as zeros
+    __device__ __forceinline__ void load(const uint16_t *__restrict__ base, int64_t stride, int r0,
+                                         int nrows, int tid) {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int idx = tid + u * NT;
+            const int row = idx / GPR, g = idx % GPR;
+            const int rr = r0 + row;
+            v[u] = rr < nrows ? *reinterpret_cast<const u32x4 *>(base + (int64_t)rr * stride + g * 8)
+                              : u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(UL_LDS unsigned char *tile, int tid) const {
+#pragma unroll
+        for (int u = 0; u < UNITS; ++u) {
+            const int idx = tid + u * NT;
+            *reinterpret_cast<UL_LDS u32x4 *>(tile + tile_off<D>(idx / GPR, idx % GPR)) = v[u];
+        }
+    }
+};
 
 }  // namespace ul
