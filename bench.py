@@ -90,6 +90,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=3, help="attention workload id (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-prefix", type=int, default=8192)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (a known-size reference for "
+                         "HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,6 +128,14 @@ def main() -> int:
     ws = torch.empty(B.workspace_bytes(wl.B, wl.N, wl.Hq, wl.Hkv, wl.d, B.UL_BF16),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev is not None:

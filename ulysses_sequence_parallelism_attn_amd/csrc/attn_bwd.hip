@@ -114,20 +114,20 @@ struct DqTile {
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_tile(f32x16 *dqacc, const bf16x8 *qf, const bf16x8 *dof,
                                         float lse2, float Drow, const UL_LDS unsigned char *kt,
-                                        const UL_LDS unsigned char *vt, const TrAddr<D> &ta, int m,
+                                        const UL_LDS unsigned char *vt, const FragOffs<D> &o,
                                         int kg, int j0, int row, int N, int causal, float c) {
-    constexpr int KK = D / 16, EB = D / 32;
-    const int krow = kperm(m);
+    constexpr int KK = D / 16, EB = D / 32, ROWB = D * 2;
 #pragma unroll
     for (int js = 0; js < 2; ++js) {
+        const UL_LDS unsigned char *kj = kt + js * 32 * ROWB, *vj = vt + js * 32 * ROWB;
         f32x16 s = zero16(), dp = zero16();
-        bf16x8 ak = row_frag<D>(kt, js * 32 + krow, kg), av = row_frag<D>(vt, js * 32 + krow, kg);
+        bf16x8 ak = lds_frag(kj, o.rm[0]), av = lds_frag(vj, o.rm[0]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             bf16x8 nk = ak, nv = av;
             if (kk + 1 < KK) {
-                nk = row_frag<D>(kt, js * 32 + krow, (kk + 1) * 2 + kg);
-                nv = row_frag<D>(vt, js * 32 + krow, (kk + 1) * 2 + kg);
+                nk = lds_frag(kj, o.rm[kk + 1]);
+                nv = lds_frag(vj, o.rm[kk + 1]);
             }
             s = mfma32x32x16(ak, qf[kk], s);
             dp = mfma32x32x16(av, dof[kk], dp);
@@ -151,12 +151,16 @@ __device__ __forceinline__ void dq_tile(f32x16 *dqacc, const bf16x8 *qf, const b
             }
             dsf[hh] = pack8(ds);
         }
-        bf16x8 a = tr_frag<D>(kt, ta, js * 32, 0);
+        // dQ^T += K^T dS^T over this half's 32 keys (2 k-steps of 16)
+        bf16x8 a = lds_tr_frag(kj, o.tr[0][0], o.tr[0][1]);
 #pragma unroll
         for (int st = 0; st < 2 * EB; ++st) {
             const int hh = st / EB, eb = st % EB;
             bf16x8 n = a;
-            if (st + 1 < 2 * EB) n = tr_frag<D>(kt, ta, js * 32 + ((st + 1) / EB) * 16, ((st + 1) % EB) * 32);
+            if (st + 1 < 2 * EB) {
+                const int nh = (st + 1) / EB, ne = (st + 1) % EB;
+                n = lds_tr_frag(kj + nh * 16 * ROWB, o.tr[ne][0], o.tr[ne][1]);
+            }
             dqacc[eb] = mfma32x32x16(a, dsf[hh], dqacc[eb]);
             a = n;
             __builtin_amdgcn_sched_barrier(0);
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const int ntiles = (kend + kKT - 1) / kKT;
     const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
     const float c = p.scale_log2;
-    const TrAddr<D> ta(lane);
+    const FragOffs<D> fo(lane);
 
     TileStage<D, kKT, kQThreads> sk, sv;
     sk.load(kb, kv_rs, 0, N, tid);
@@ -236,9 +240,9 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
         const UL_LDS unsigned char *vt = kt + T::kBytes;
         if constexpr (decltype(masked)::value) {
             if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
-                dq_tile<D, true>(dqacc, qf, dof, lse2, Drow, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+                dq_tile<D, true>(dqacc, qf, dof, lse2, Drow, kt, vt, fo, kg, j0, row, N, p.causal, c);
         } else {
-            dq_tile<D, false>(dqacc, qf, dof, lse2, Drow, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+            dq_tile<D, false>(dqacc, qf, dof, lse2, Drow, kt, vt, fo, kg, j0, row, N, p.causal, c);
         }
         if (t + 1 < ntiles) {
             UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;
@@ -283,19 +287,27 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 
 // ============================================================================ bf16: dK/dV kernel
 //
-// 4 waves (one per SIMD, the full register file each), 32 keys per wave, 128
-// keys per workgroup for one KV head; steps over 64-row query tiles of every
-// query head of the group, from the causal diagonal to N.  Per step:
-//   S  = Q K^T,  dP = dO V^T     (A = Q / dO rows from LDS, B = K / V fragments in registers)
-//   P = exp2(S c - lse2), dS = P (dP - D)   (lane column = key, registers = query rows)
-//   dV^T += dO^T P,  dK^T += Q^T dS         (A = dO^T / Q^T by transposed LDS reads)
-// dK and dV are summed over the group's query heads in registers.
+// 8 waves per workgroup, 128 keys of one KV head: waves 0-3 are producers and
+// waves 4-7 consumers; producer w and consumer w+4 share a SIMD and own the
+// same 32 keys.  The workgroup steps over 32-row query tiles of every query
+// head of the group, from the causal diagonal to N.
+//   producer, step s:  S = Q K^T, dP = dO V^T   (A = Q / dO rows from LDS,
+//                      B = K / V fragments held in registers), P = exp2(S c - lse2),
+//                      dS = P (dP - D); the bf16 P and dS fragments go to LDS
+//                      in the lane order of the consumer's B operand.
+//   consumer, step s-1: dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T by
+//                      transposed LDS reads), summed over the group's heads.
+// The producer's softmax VALU work overlaps the consumer's MFMAs on the same
+// SIMD, and each role stays inside a 256-register budget (2 waves per SIMD).
+// Q/dO tiles rotate through 3 LDS stages (being filled / produced / consumed);
+// P/dS through 2.
 
-constexpr int kKvWaves = 4;
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
+constexpr int kKvPairs = 4;                          // producer/consumer pairs
 constexpr int kKeysPerWave = 32;
-constexpr int kKeysPerWg = kKvWaves * kKeysPerWave;  // 128
-constexpr int kQT = 64;                              // query rows per step
+constexpr int kKeysPerWg = kKvPairs * kKeysPerWave;  // 128
+constexpr int kQT = 32;                              // query rows per step
 
 struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
@@ -309,86 +321,115 @@ struct DkvParams {
 
 template <int D>
 struct DkvTile {
-    static constexpr int kKV = kKeysPerWg * D * 2;     // static K or V tile of the workgroup
     static constexpr int kBytes = kQT * D * 2;          // one Q or dO tile
     static constexpr int kStats = 2 * kQT * 4;          // lse2 then D, fp32
     static constexpr int kStage = 2 * kBytes + kStats;  // Q, dO, stats
-    static constexpr int kStage0 = 2 * kKV;
-    static constexpr int kLds = kStage0 + 2 * kStage;
+    static constexpr int kPds = kKvPairs * 4 * 64 * 16; // P[2], dS[2] fragments per pair, per lane
+    static constexpr int kStages = 4;                   // in flight x2 / produced / consumed
+    static constexpr int kPdsStages = 2;
+    static constexpr int kPds0 = kStages * kStage;
+    static constexpr int kLds = kPds0 + kPdsStages * kPds;
+    __device__ static constexpr int stage(int st) { return st * kStage; }
+    __device__ static constexpr int pds(int st) { return kPds0 + st * kPds; }
 };
 
-template <int D, bool MASK>
-__device__ __forceinline__ void dkdv_step(f32x16 *dkacc, f32x16 *dvacc, const UL_LDS unsigned char *kt,
-                                          const UL_LDS unsigned char *vt, int wrow,
-                                          const UL_LDS unsigned char *qt,
-                                          const UL_LDS unsigned char *dot,
-                                          const UL_LDS float *lse2s, const UL_LDS float *Ds,
-                                          const TrAddr<D> &ta, int m, int kg, int r0, int key,
-                                          int N, int causal, float c) {
-    constexpr int KK = D / 16, EB = D / 32;
-    const int qrow = kperm(m);
-    bf16x8 pf[4], dsf[4];
+// Per-lane LDS offsets used inside the step loop (see precomputed lane offsets).
+template <int D>
+struct DkvOffs {
+    static constexpr int KK = D / 16, EB = D / 32;
+    uint32_t rm[KK];      // producer: Q / dO row fragment of k-step kk (row kperm(m))
+    uint32_t stat;        // producer: first of the 8 statistics rows of this lane group
+    uint32_t pds;         // both: this lane's P/dS fragment slot in its pair's block
+    uint32_t tr[EB][2];   // consumer: transposed Q / dO fragment halves, rows 0..15
+    __device__ __forceinline__ DkvOffs(int lane, int pair) {
+        const int m = lane & 31, kg = lane >> 5;
+        const int qrow = kperm(m);
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-        f32x16 s = zero16(), dp = zero16();
-        // A = Q / dO rows (kperm order), B = this wave's K / V rows (column = key)
-        bf16x8 aq = row_frag<D>(qt, ib * 32 + qrow, kg), ad = row_frag<D>(dot, ib * 32 + qrow, kg);
-        bf16x8 bk = row_frag<D>(kt, wrow, kg), bv = row_frag<D>(vt, wrow, kg);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 nq = aq, nd = ad, nk = bk, nv = bv;
-            if (kk + 1 < KK) {
-                const int g = (kk + 1) * 2 + kg;
-                nq = row_frag<D>(qt, ib * 32 + qrow, g);
-                nd = row_frag<D>(dot, ib * 32 + qrow, g);
-                nk = row_frag<D>(kt, wrow, g);
-                nv = row_frag<D>(vt, wrow, g);
-            }
-            s = mfma32x32x16(aq, bk, s);
-            dp = mfma32x32x16(ad, bv, dp);
-            aq = nq;
-            ad = nd;
-            bk = nk;
-            bv = nv;
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // C register r of lane group kg holds query row ib*32 + ckey(r, kg):
-        // runs of 8 consecutive rows, so the row statistics load as float4s.
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int rb = ib * 32 + hh * 16 + kg * 8;
-            const f32x4 l0 = *reinterpret_cast<const UL_LDS f32x4 *>(lse2s + rb);
-            const f32x4 l1 = *reinterpret_cast<const UL_LDS f32x4 *>(lse2s + rb + 4);
-            const f32x4 d0 = *reinterpret_cast<const UL_LDS f32x4 *>(Ds + rb);
-            const f32x4 d1 = *reinterpret_cast<const UL_LDS f32x4 *>(Ds + rb + 4);
-            float pv[8], dsv[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int r = hh * 8 + q;
-                const float lz = q < 4 ? l0[q] : l1[q - 4];
-                const float dz = q < 4 ? d0[q] : d1[q - 4];
-                float pz = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
-                if constexpr (MASK) {
-                    const int i = r0 + rb + q;
-                    if (i >= N || key >= N || (causal && key > i)) pz = 0.f;
-                }
-                pv[q] = pz;
-                dsv[q] = pz * (dp[r] - dz);
-            }
-            pf[ib * 2 + hh] = pack8(pv);
-            dsf[ib * 2 + hh] = pack8(dsv);
-        }
-    }
-    // dV^T += dO^T P ; dK^T += Q^T dS   (k = query rows, 4 steps of 16)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+        for (int kk = 0; kk < KK; ++kk) rm[kk] = rm_off<D>(qrow, kk * 2 + kg);
+        stat = 2 * DkvTile<D>::kBytes + kg * 8 * 4;
+        pds = (uint32_t)(pair * 4 * 64 + lane) * 16;
+        const TrAddr<D> ta(lane);
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb) {
-            const bf16x8 ado = tr_frag<D>(dot, ta, ks * 16, eb * 32);
-            const bf16x8 aq = tr_frag<D>(qt, ta, ks * 16, eb * 32);
+            tr[eb][0] = tr_off<D>(ta, eb * 32, 0);
+            tr[eb][1] = tr_off<D>(ta, eb * 32, 1);
+        }
+    }
+};
+
+// Producer step on the Q/dO tile at `tile` (stage base): S, dP -> P, dS
+// fragments (masked per MASK) -> the P/dS block at `pdsb`.
+template <int D, bool MASK>
+__device__ __forceinline__ void dkdv_produce(const bf16x8 *kf, const bf16x8 *vf,
+                                             const UL_LDS unsigned char *tile, UL_LDS unsigned char *pdsb,
+                                             const DkvOffs<D> &o, int kg, int r0, int key, int N,
+                                             int causal, float c) {
+    using T = DkvTile<D>;
+    constexpr int KK = D / 16;
+    f32x16 s = zero16(), dp = zero16();
+    bf16x8 aq = lds_frag(tile, o.rm[0]), ad = lds_frag(tile + T::kBytes, o.rm[0]);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 nq = aq, nd = ad;
+        if (kk + 1 < KK) {
+            nq = lds_frag(tile, o.rm[kk + 1]);
+            nd = lds_frag(tile + T::kBytes, o.rm[kk + 1]);
+        }
+        s = mfma32x32x16(aq, kf[kk], s);
+        dp = mfma32x32x16(ad, vf[kk], dp);
+        aq = nq;
+        ad = nd;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // C register r of lane group kg holds query row ckey(r, kg): two runs of 8
+    // consecutive rows (16*hh + 8*kg ..), so the row statistics load as float4s.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const UL_LDS unsigned char *st = tile + o.stat + hh * 16 * 4;
+        const f32x4 l0 = *reinterpret_cast<const UL_LDS f32x4 *>(st);
+        const f32x4 l1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + 16);
+        const f32x4 d0 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4);
+        const f32x4 d1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4 + 16);
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = hh * 8 + q;
+            const float lz = q < 4 ? l0[q] : l1[q - 4];
+            const float dz = q < 4 ? d0[q] : d1[q - 4];
+            float pz = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
+            if constexpr (MASK) {
+                const int i = r0 + hh * 16 + kg * 8 + q;
+                if (i >= N || key >= N || (causal && key > i)) pz = 0.f;
+            }
+            pv[q] = pz;
+            dsv[q] = pz * (dp[r] - dz);
+        }
+        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + hh * 64 * 16) = __builtin_bit_cast(u32x4, pack8(pv));
+        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + (2 + hh) * 64 * 16) = __builtin_bit_cast(u32x4, pack8(dsv));
+    }
+}
+
+// Consumer step: dV^T += dO^T P ; dK^T += Q^T dS  (k = query rows, 2 steps of 16)
+template <int D>
+__device__ __forceinline__ void dkdv_consume(f32x16 *dkacc, f32x16 *dvacc, const UL_LDS unsigned char *tile,
+                                             const UL_LDS unsigned char *pdsb, const DkvOffs<D> &o) {
+    using T = DkvTile<D>;
+    constexpr int EB = D / 32;
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        pf[hh] = lds_frag(pdsb, o.pds + hh * 64 * 16);
+        dsf[hh] = lds_frag(pdsb, o.pds + (2 + hh) * 64 * 16);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+            const int rofs = ks * 16 * D * 2;
+            const bf16x8 ado = lds_tr_frag(tile + T::kBytes + rofs, o.tr[eb][0], o.tr[eb][1]);
+            const bf16x8 aq = lds_tr_frag(tile + rofs, o.tr[eb][0], o.tr[eb][1]);
             dvacc[eb] = mfma32x32x16(ado, pf[ks], dvacc[eb]);
             dkacc[eb] = mfma32x32x16(aq, dsf[ks], dkacc[eb]);
-            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -398,9 +439,12 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     extern __shared__ __align__(16) unsigned char smem_raw[];
     UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
     using T = DkvTile<D>;
+    using Tile = DmaTile<D, kQT>;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
+    const bool producer = wave < kKvPairs;
+    const int pair = producer ? wave : wave - kKvPairs;
 
     // item = kblk * (B*Hkv) + (b*Hkv + g): key block 0 (the most work) first
     const int per_rank = p.B * p.Hkv;
@@ -409,94 +453,131 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
     const int N = p.N;
-    const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
+    const int64_t q_rs = (int64_t)p.Hq * D;
     const int kb0 = kblk * kKeysPerWg;
-    const int wrow = wave * kKeysPerWave + m;   // this lane's key row in the static tiles
-    const int jw0 = kb0 + wave * kKeysPerWave;  // this wave's first key
-    const int key = kb0 + wrow;                 // this lane's key (C column)
+    const int jw0 = kb0 + pair * kKeysPerWave;  // the pair's first key
+    const int key = jw0 + m;                    // this lane's key (C column)
+
+    // Steps: 32-row tiles from the end of the sequence down to the causal
+    // diagonal, the group's query heads innermost.  Every workgroup walks the
+    // rows in the same order, so workgroups resident at the same time stream
+    // the same Q/dO tiles and share them through L2.
+    const int qt_first = p.causal ? kb0 / kQT : 0;
+    const int nqt = (N + kQT - 1) / kQT;
+    const int per_head = nqt - qt_first;
+    const int nsteps = per_head * grp;
+    auto row0 = [&](int s) { return (nqt - 1 - s / grp) * kQT; };
+    auto head = [&](int s) { return g * grp + s % grp; };
+    const float c = p.scale_log2;
+    const DkvOffs<D> o(lane, pair);
+
+    // Direct loads of step s into LDS stage s % 4: the Q and dO tiles are
+    // split evenly over the 8 waves; wave 0 also fetches the 32 lse2 and D
+    // values (one dword per lane).
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvWaves;  // per step, waves 1..7
+    static_assert(2 * Tile::INSTR % kKvWaves == 0, "Q and dO tiles split evenly over the waves");
+    auto issue_step = [&](int s, UL_LDS unsigned char *base) {
+        const int h = head(s), r0 = row0(s);
+        const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
+        const uint16_t *db = p.dout + ((int64_t)b * N * p.Hq + h) * D;
+#pragma unroll
+        for (int k = 0; k < kDmaPerWave; ++k) {
+            const int u = wave * kDmaPerWave + k;  // 0 .. 2*INSTR-1: Q tile first, then dO
+            if (u < Tile::INSTR)
+                Tile::issue(qb, q_rs, r0, N, base, u, lane);
+            else
+                Tile::issue(db, q_rs, r0, N, base + T::kBytes, u - Tile::INSTR, lane);
+        }
+        if (wave == 0) {
+            const int i = min(r0 + (lane & (kQT - 1)), N - 1);
+            const float *src = (lane < kQT ? p.lse2 : p.Dv) + ((int64_t)b * p.Hq + h) * N + i;
+            dma_b32(src, base + 2 * T::kBytes);
+        }
+    };
+    // the pair's keys see at least one row of step s
+    auto visible = [&](int s) { return (!p.causal || jw0 <= row0(s) + kQT - 1) && jw0 < N; };
+
+    if (nsteps > 0) issue_step(0, lds + T::stage(0));
+    if (nsteps > 1) issue_step(1, lds + T::stage(1));
+    __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+
+    // Iteration i (LDS stage i % 4, unrolled by 4 so stages are immediates):
+    // issue step i+2, producers handle step i, consumers step i-1; the
+    // barrier at the end waits for step i+1 (older than step i+2's loads).
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    auto run = [&](auto body) {
+        int i = 0;
+        for (; i + 4 <= nsteps + 1; i += 4) {
+            body(i, S0{});
+            body(i + 1, S1{});
+            body(i + 2, S2{});
+            body(i + 3, S3{});
+        }
+        if (i <= nsteps) body(i, S0{});
+        if (i + 1 <= nsteps) body(i + 1, S1{});
+        if (i + 2 <= nsteps) body(i + 2, S2{});
+    };
+    auto finish = [&](int i) {
+        if (i + 2 < nsteps)
+            wait_vm_barrier<kDmaPerWave>();
+        else
+            wait_vm_barrier<0>();
+    };
+
+    if (producer) {
+        // K and V rows of the pair's 32 keys as B fragments (column = key, k = head dim)
+        constexpr int KK = D / 16;
+        bf16x8 kf[KK], vf[KK];
+        {
+            const bool ok = key < N;
+            const uint16_t *kr = p.k + (((int64_t)b * N + (ok ? key : 0)) * p.Hkv + g) * D;
+            const uint16_t *vr = p.v + (((int64_t)b * N + (ok ? key : 0)) * p.Hkv + g) * D;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(kr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
+                vf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(vr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
+            }
+        }
+        // Retire these loads here: inside the loop vmcnt must count only the
+        // stage loads, or a wait for a fragment would also wait for the
+        // newest stage.
+        __builtin_amdgcn_s_waitcnt(0x70);
+        run([&](int i, auto stage) {
+            constexpr int ST = decltype(stage)::value, NN = (ST + 2) % 4, PD = ST % 2;
+            if (i + 2 < nsteps) issue_step(i + 2, lds + T::stage(NN));
+            if (i < nsteps && visible(i)) {
+                const int r0 = row0(i);
+                const bool full = (!p.causal || r0 >= kb0 + kKeysPerWg) && r0 + kQT <= N &&
+                                  kb0 + kKeysPerWg <= N;
+                if (full)
+                    dkdv_produce<D, false>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, r0, key,
+                                           N, p.causal, c);
+                else
+                    dkdv_produce<D, true>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, r0, key,
+                                          N, p.causal, c);
+            }
+            finish(i);
+        });
+        return;
+    }
 
     constexpr int EB = D / 32;
-    {
-        const uint16_t *kb = p.k + ((int64_t)b * N * p.Hkv + g) * D;
-        const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
-        TileStage<D, kKeysPerWg, kKvThreads> sk;
-        sk.load(kb, kv_rs, kb0, N, tid);
-        sk.store(lds, tid);
-        sk.load(vb, kv_rs, kb0, N, tid);
-        sk.store(lds + T::kKV, tid);
-    }
-    const UL_LDS unsigned char *kt = lds, *vt = lds + T::kKV;
     f32x16 dkacc[EB], dvacc[EB];
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
         dkacc[eb] = zero16();
         dvacc[eb] = zero16();
     }
-
-    // Steps: every query head of the group x 64-row tiles from the diagonal.
-    // A step needs no mask when its rows all lie at or after the workgroup's
-    // last key and inside N.
-    const int qt_first = p.causal ? kb0 / kQT : 0;
-    const int nqt = (N + kQT - 1) / kQT;
-    const int per_head = nqt - qt_first;
-    const int nsteps = per_head * grp;
-    const float c = p.scale_log2;
-    const TrAddr<D> ta(lane);
-
-    TileStage<D, kQT, kKvThreads> sq, sd;
-    float stat = 0.f;  // lse2 (tid < 64) or D (64 <= tid < 128) of one row
-    auto load_step = [&](int s) {
-        const int h = g * grp + s / per_head;
-        const int r0 = (qt_first + s % per_head) * kQT;
-        const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
-        const uint16_t *db = p.dout + ((int64_t)b * N * p.Hq + h) * D;
-        sq.load(qb, q_rs, r0, N, tid);
-        sd.load(db, q_rs, r0, N, tid);
-        if (tid < 2 * kQT) {
-            const int i = r0 + (tid & (kQT - 1));
-            const int64_t so = ((int64_t)b * p.Hq + h) * N + i;
-            stat = i < N ? ((tid < kQT) ? p.lse2[so] : p.Dv[so]) : 0.f;
-        }
-    };
-    auto store_step = [&](UL_LDS unsigned char *base) {
-        sq.store(base, tid);
-        sd.store(base + T::kBytes, tid);
-        if (tid < 2 * kQT) reinterpret_cast<UL_LDS float *>(base + 2 * T::kBytes)[tid] = stat;
-    };
-
-    if (nsteps > 0) {
-        load_step(0);
-        store_step(lds + T::kStage0);
-    }
-    __syncthreads();
-
-    auto step = [&](int s, auto stage) {
-        constexpr int st = decltype(stage)::value;
-        const int r0 = (qt_first + s % per_head) * kQT;
-        if (s + 1 < nsteps) load_step(s + 1);
-        const UL_LDS unsigned char *base = lds + T::kStage0 + st * T::kStage;
-        const UL_LDS unsigned char *qt = base, *dot = base + T::kBytes;
-        const UL_LDS float *lse2s = reinterpret_cast<const UL_LDS float *>(base + 2 * T::kBytes);
-        const UL_LDS float *Ds = lse2s + kQT;
-        const bool full = (!p.causal || r0 >= kb0 + kKeysPerWg) && r0 + kQT <= N && kb0 + kKeysPerWg <= N;
-        if (full) {
-            dkdv_step<D, false>(dkacc, dvacc, kt, vt, wrow, qt, dot, lse2s, Ds, ta, m, kg, r0, key, N,
-                                p.causal, c);
-        } else if ((!p.causal || jw0 <= r0 + kQT - 1) && jw0 < N) {
-            dkdv_step<D, true>(dkacc, dvacc, kt, vt, wrow, qt, dot, lse2s, Ds, ta, m, kg, r0, key, N,
-                               p.causal, c);
-        }
-        if (s + 1 < nsteps) store_step(lds + T::kStage0 + (st ^ 1) * T::kStage);
-        __syncthreads();
-    };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-        step(s, S0{});
-        step(s + 1, S1{});
-    }
-    if (s < nsteps) step(s, S0{});
+    run([&](int i, auto stage) {
+        constexpr int ST = decltype(stage)::value, NN = (ST + 2) % 4, PV = (ST + 3) % 4, PD = (ST + 1) % 2;
+        if (i + 2 < nsteps) issue_step(i + 2, lds + T::stage(NN));
+        if (i >= 1 && visible(i - 1)) dkdv_consume<D>(dkacc, dvacc, lds + T::stage(PV), lds + T::pds(PD), o);
+        finish(i);
+    });
 
     // dK = scale * acc, dV = acc (bf16); lane column = key, registers = head dim
     if (key < N) {

@@ -84,22 +84,20 @@ struct FwdAcc {
 template <int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
                                          const UL_LDS unsigned char *kt,
-                                         const UL_LDS unsigned char *vt, const TrAddr<D> &ta,
-                                         int m, int kg, int j0, int row, int N, int causal,
-                                         float c) {
-    constexpr int KK = D / 16, EB = D / 32;
+                                         const UL_LDS unsigned char *vt, const FragOffs<D> &o,
+                                         int kg, int j0, int row, int N, int causal, float c) {
+    constexpr int KK = D / 16, EB = D / 32, HALF = 32 * D * 2;
     // S^T: one k-step of fragments in flight ahead of the MFMAs that use them
     // (the barrier stops the scheduler from hoisting every LDS read of the
     // tile, which would not fit in the register budget of 2 waves per SIMD).
     f32x16 s[2] = {zero16(), zero16()};
-    const int krow = kperm(m);
-    bf16x8 a0 = row_frag<D>(kt, krow, kg), a1 = row_frag<D>(kt, 32 + krow, kg);
+    bf16x8 a0 = lds_frag(kt, o.rm[0]), a1 = lds_frag(kt + HALF, o.rm[0]);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         bf16x8 n0 = a0, n1 = a1;
         if (kk + 1 < KK) {
-            n0 = row_frag<D>(kt, krow, (kk + 1) * 2 + kg);
-            n1 = row_frag<D>(kt, 32 + krow, (kk + 1) * 2 + kg);
+            n0 = lds_frag(kt, o.rm[kk + 1]);
+            n1 = lds_frag(kt + HALF, o.rm[kk + 1]);
         }
         s[0] = mfma32x32x16(a0, qf[kk], s[0]);
         s[1] = mfma32x32x16(a1, qf[kk], s[1]);
@@ -152,12 +150,15 @@ __device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
     acc.l += ls;
 
     // O^T += V^T P^T, same one-step lookahead
-    bf16x8 va = tr_frag<D>(vt, ta, 0, 0);
+    bf16x8 va = lds_tr_frag(vt, o.tr[0][0], o.tr[0][1]);
 #pragma unroll
     for (int step = 0; step < 4 * EB; ++step) {
         const int kap = step / EB, eb = step % EB;
         bf16x8 vn = va;
-        if (step + 1 < 4 * EB) vn = tr_frag<D>(vt, ta, ((step + 1) / EB) * 16, ((step + 1) % EB) * 32);
+        if (step + 1 < 4 * EB) {
+            const int nk = (step + 1) / EB, ne = (step + 1) % EB;
+            vn = lds_tr_frag(vt + nk * 16 * D * 2, o.tr[ne][0], o.tr[ne][1]);
+        }
         acc.o[eb] = mfma32x32x16(va, pf[kap], acc.o[eb]);
         va = vn;
         __builtin_amdgcn_sched_barrier(0);
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const int ntiles = (kend + kKT - 1) / kKT;
     const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
     const float c = p.scale_log2;
-    const TrAddr<D> ta(lane);
+    const FragOffs<D> fo(lane);
 
     TileStage<D, kKT, kThreads> sk, sv;
     sk.load(kb, kv_rs, 0, N, tid);
@@ -239,9 +240,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
         const UL_LDS unsigned char *vt = kt + T::kBytes;
         if constexpr (decltype(masked)::value) {
             if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
-                fwd_tile<D, true>(acc, qf, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+                fwd_tile<D, true>(acc, qf, kt, vt, fo, kg, j0, row, N, p.causal, c);
         } else {
-            fwd_tile<D, false>(acc, qf, kt, vt, ta, m, kg, j0, row, N, p.causal, c);
+            fwd_tile<D, false>(acc, qf, kt, vt, fo, kg, j0, row, N, p.causal, c);
         }
         if (t + 1 < ntiles) {
             UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;

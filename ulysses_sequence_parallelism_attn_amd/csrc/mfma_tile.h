@@ -44,7 +44,7 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8 &a, const bf16x8 &b,
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
@@ -144,14 +144,75 @@ __device__ __forceinline__ bf16x8 tr_frag(const UL_LDS unsigned char *tile, cons
     return r;
 }
 
+// ---------------------------------------------------------------- precomputed lane offsets
+//
+// Fragment addresses depend on the lane only through the XOR swizzle, so each
+// kernel computes them once; inside the loops an address is then one of these
+// registers plus a compile-time byte offset (the LDS stage, the tile within
+// the stage, and a row block that is a multiple of 16 rows, which leaves the
+// swizzle unchanged), which the ds_read instructions take as an immediate.
+
+// Row read of granule g of row r (r's swizzle class is r & 15).
+template <int D>
+__device__ __forceinline__ uint32_t rm_off(int r, int g) { return (uint32_t)tile_off<D>(r, g); }
+
+// The two halves of a transposed fragment at rows [8*kg + 4*half + j/4] and
+// columns c0 + col_off (c0 a multiple of 32); rows advance in multiples of 16.
+template <int D>
+__device__ __forceinline__ uint32_t tr_off(const TrAddr<D> &ta, int c0, int half) {
+    const int c = c0 + ta.col_off;
+    const int r = ta.row_off + 4 * half;
+    return (uint32_t)(tile_off<D>(r, c >> 3) + ((c & 7) << 1));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const UL_LDS unsigned char *base, uint32_t off) {
+    const u32x4 v = *reinterpret_cast<const UL_LDS u32x4 *>(base + off);
+    return as_bf16x8(v);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr_frag(const UL_LDS unsigned char *base, uint32_t off_lo,
+                                              uint32_t off_hi) {
+    const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((UL_LDS v4bf16 *)(base + off_lo));
+    const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((UL_LDS v4bf16 *)(base + off_hi));
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+// Offsets of the two fragment kinds every attention kernel reads from a
+// [rows][D] tile: row fragments of row kperm(m) (+ multiples of 32 rows) for
+// k-step kk, and transposed fragments for column block eb (+ multiples of 16
+// rows).
+template <int D>
+struct FragOffs {
+    static constexpr int KK = D / 16, EB = D / 32;
+    uint32_t rm[KK];
+    uint32_t tr[EB][2];
+    __device__ __forceinline__ explicit FragOffs(int lane) {
+        const int m = lane & 31, kg = lane >> 5;
+        const int prow = kperm(m);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) rm[kk] = rm_off<D>(prow, kk * 2 + kg);
+        const TrAddr<D> ta(lane);
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb) {
+            tr[eb][0] = tr_off<D>(ta, eb * 32, 0);
+            tr[eb][1] = tr_off<D>(ta, eb * 32, 1);
+        }
+    }
+};
+
 // Cooperative tile staging: NT threads move ROWS x D bf16 between global
 // memory (row stride `stride` elements) and a swizzled LDS tile, 16 bytes per
-// lane per unit, consecutive lanes on consecutive granules of a row.
+// lane per unit, consecutive lanes on consecutive granules of a row.  When the
+// tile has fewer granules than threads, the surplus threads move nothing.
 template <int D, int ROWS, int NT>
 struct TileStage {
-    static constexpr int GPR = D / 8;                 // granules per row
-    static constexpr int UNITS = ROWS * GPR / NT;     // granules per thread
-    static_assert(ROWS * GPR % NT == 0, "tile must divide evenly among threads");
+    static constexpr int GPR = D / 8;                          // granules per row
+    static constexpr int TOTAL = ROWS * GPR;                   // granules per tile
+    static constexpr int UNITS = (TOTAL + NT - 1) / NT;        // granules per thread
+    static_assert(TOTAL % NT == 0 || TOTAL < NT, "tile must divide evenly among threads");
     u32x4 v[UNITS];
 
     // rows r0 + row >= nrows read as zeros
@@ -162,17 +223,76 @@ struct TileStage {
             const int idx = tid + u * NT;
             const int row = idx / GPR, g = idx % GPR;
             const int rr = r0 + row;
-            v[u] = rr < nrows ? *reinterpret_cast<const u32x4 *>(base + (int64_t)rr * stride + g * 8)
-                              : u32x4{0, 0, 0, 0};
+            v[u] = (idx < TOTAL && rr < nrows)
+                       ? *reinterpret_cast<const u32x4 *>(base + (int64_t)rr * stride + g * 8)
+                       : u32x4{0, 0, 0, 0};
         }
     }
     __device__ __forceinline__ void store(UL_LDS unsigned char *tile, int tid) const {
 #pragma unroll
         for (int u = 0; u < UNITS; ++u) {
             const int idx = tid + u * NT;
-            *reinterpret_cast<UL_LDS u32x4 *>(tile + tile_off<D>(idx / GPR, idx % GPR)) = v[u];
+            if (TOTAL % NT == 0 || idx < TOTAL)
+                *reinterpret_cast<UL_LDS u32x4 *>(tile + tile_off<D>(idx / GPR, idx % GPR)) = v[u];
         }
     }
 };
+
+// ---------------------------------------------------------------- direct global -> LDS tiles
+//
+// global_load_lds_dwordx4 writes the 16 bytes of lane L at M0 + 16*L: one wave
+// instruction fills 1 KB of LDS.  Wave instruction u of a tile covers bytes
+// [1024u, 1024u + 1024) of the swizzled layout, so lane L fetches the granule
+// the layout keeps at slot 64u + L.  Rows at or past `nrows` are read from row
+// nrows - 1 instead (in bounds; the kernels mask those rows).
+//
+// The loads are issued from inline assembly so that the compiler does not
+// treat them as LDS stores of unknown extent and wait for them before every
+// LDS read; their completion is awaited explicitly (wait_vm_barrier) before
+// the barrier that publishes a stage.  vmcnt retires loads in order, so the
+// compiler's own waits for ordinary loads can only become more conservative.
+__device__ __forceinline__ uint32_t lds_addr(const UL_LDS void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+__device__ __forceinline__ void dma_b128(const void *gsrc, const UL_LDS void *ldst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_addr(ldst)), "v"(gsrc)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma_b32(const void *gsrc, const UL_LDS void *ldst) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_addr(ldst)), "v"(gsrc)
+                 : "memory", "m0");
+}
+
+template <int D, int ROWS>
+struct DmaTile {
+    static constexpr int ROWB = D * 2, GPR = D / 8;
+    static constexpr int INSTR = ROWS * ROWB / 1024;     // wave instructions per tile
+    static constexpr int ROWS_PER_INSTR = 1024 / ROWB;
+    static_assert(ROWS * ROWB % 1024 == 0, "tile must be a whole number of KB");
+
+    __device__ static __forceinline__ void issue(const uint16_t *gbase, int64_t stride, int r0, int nrows,
+                                                 UL_LDS unsigned char *tile, int u, int lane) {
+        const int r = u * ROWS_PER_INSTR + lane / GPR;
+        const int g = (lane % GPR) ^ swz<D>(r);
+        const int rr = min(r0 + r, nrows - 1);
+        dma_b128(gbase + (int64_t)rr * stride + g * 8, tile + u * 1024);
+    }
+};
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all of its LDS operations are done, then meet the other
+// waves (s_waitcnt encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x70 | N);
+    asm volatile("s_barrier" ::: "memory");
+}
 
 }  // namespace ul
