@@ -10,6 +10,10 @@ One step is one pass of the whole path over one batch of synthetic input:
   3. ul_attn_bwd: its dQ, dK, dV;
   4. ul_relayout_h2s of the [3, 4, 65536, 8, 128] head-sharded stack (the reverse exchange).
 
+The backward runs as its three C-ABI stages (D/lse preparation, the dQ pass, the dK/dV
+pass) with events between them, so each kernel's duration is measured on the stream it
+runs on; the `roofline` object reports the longest one against its peak.
+
 The headline value is counted attention FLOPs per second over whole steps: causal
 forward 2*N^2*Hq*d plus backward 2.5x that (7*N^2*Hq*d per step), in TFLOP/s.  The
 relayouts add time but no FLOPs.  Inputs are resident in HBM before timing starts.
@@ -57,6 +61,59 @@ def measured_traffic(kernel: str) -> float | None:
     return float(v) if v is not None else None
 
 
+# rocprofv3 kernel names -> the names used in the roofline objects
+KERNEL_NAMES = [
+    ("relayout32_kernel<unsigned int __vector(4), true>", "relayout_s2h"),
+    ("relayout32_kernel<unsigned int __vector(4), false>", "relayout_h2s"),
+    ("attn_fwd_bf16_kernel<128>", "attn_fwd"),
+    ("bwd_pre_kernel", "attn_bwd_prep"),
+    ("attn_bwd_dq_bf16_kernel<128>", "attn_bwd_dq"),
+    ("attn_bwd_dkdv_bf16_kernel<128>", "attn_bwd_dkdv"),
+]
+CALIBRATION_KERNEL = "__amd_rocclr_copyBuffer"
+CALIBRATION_BYTES = float(1 << 30)
+
+
+def _pmc_per_kernel(csv_path: Path, counter: str) -> dict:
+    """Mean counter value per dispatch for each known kernel (and the calibration copy)."""
+    import csv
+
+    acc: dict = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        key = CALIBRATION_KERNEL if CALIBRATION_KERNEL in name else None
+        for pat, short in KERNEL_NAMES:
+            if pat in name:
+                key = short
+        if key is None:
+            continue
+        acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_pmc(fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch),
+    each scaled by what the same counter reads for the 1 GiB calibration copy."""
+    fetch = _pmc_per_kernel(next(Path(fetch_dir).rglob("*counter_collection.csv")), "FETCH_SIZE")
+    write = _pmc_per_kernel(next(Path(write_dir).rglob("*counter_collection.csv")), "WRITE_SIZE")
+    f_cal = CALIBRATION_BYTES / (fetch[CALIBRATION_KERNEL] * 1024.0)
+    w_cal = CALIBRATION_BYTES / (write[CALIBRATION_KERNEL] * 1024.0)
+    rec = {"kernel_hash": kernel_hash(),
+           "calibration": {"kernel": CALIBRATION_KERNEL, "bytes": CALIBRATION_BYTES,
+                           "fetch_kib": fetch[CALIBRATION_KERNEL], "write_kib": write[CALIBRATION_KERNEL],
+                           "fetch_factor": f_cal, "write_factor": w_cal},
+           "fetch_bytes": {}, "write_bytes": {}, "bytes_per_launch": {}}
+    for _, short in KERNEL_NAMES:
+        if short in fetch and short in write:
+            fb, wb = fetch[short] * 1024.0 * f_cal, write[short] * 1024.0 * w_cal
+            rec["fetch_bytes"][short] = fb
+            rec["write_bytes"][short] = wb
+            rec["bytes_per_launch"][short] = fb + wb
+    return rec
+
+
 def cpu_baseline(st: dict, wl, n_prefix: int) -> dict:
     """Time the float64 oracle on a causal prefix of the workload's own inputs."""
     import numpy as np
@@ -89,11 +146,21 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="attention workload id (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-prefix", type=int, default=8192)
+    ap.add_argument("--cpu-prefix", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
                          "HBM byte counters)")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
+                         "(FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration) and exit")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        rec = ingest_pmc(*args.ingest_pmc)
+        TRAFFIC_FILE.parent.mkdir(exist_ok=True)
+        TRAFFIC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec["bytes_per_launch"]))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -137,27 +204,39 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    # One step: relayout s2h, forward, the backward's three stages, relayout h2s.  The
+    # backward runs as its three C-ABI stages (exactly what ul_attn_bwd launches) so that
+    # each kernel is bracketed by its own events on the stream it is launched on.
+    names = ["relayout_s2h", "attn_fwd", "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkdv",
+             "relayout_h2s"]
+
+    def bwd_stage(stage):
+        return lambda: B.attn_bwd(q, k, v, o, do, lse, wl.scale, True, workspace=ws, dq=dq, dk=dk,
+                                  dv=dv, stages=stage)
+
+    calls = [
+        lambda: B.relayout_s2h(x, P, out=y),
+        lambda: B.attn_fwd(q, k, v, wl.scale, True, out=o, lse=lse),
+        bwd_stage(B.UL_BWD_PREP),
+        bwd_stage(B.UL_BWD_DQ),
+        bwd_stage(B.UL_BWD_DKDV),
+        lambda: B.relayout_h2s(y, out=x2),
+    ]
+
     def step(ev=None):
+        for j, call in enumerate(calls):
+            if ev is not None:
+                ev[j].record(stream)
+            call()
         if ev is not None:
-            ev[0].record(stream)
-        B.relayout_s2h(x, P, out=y)
-        if ev is not None:
-            ev[1].record(stream)
-        B.attn_fwd(q, k, v, wl.scale, True, out=o, lse=lse)
-        if ev is not None:
-            ev[2].record(stream)
-        B.attn_bwd(q, k, v, o, do, lse, wl.scale, True, workspace=ws, dq=dq, dk=dk, dv=dv)
-        if ev is not None:
-            ev[3].record(stream)
-        B.relayout_h2s(y, out=x2)
-        if ev is not None:
-            ev[4].record(stream)
+            ev[len(calls)].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -169,36 +248,47 @@ def main() -> int:
 
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    parts = {"relayout_s2h": [], "attn_fwd": [], "attn_bwd": [], "relayout_h2s": []}
-    for e in evs:
-        for j, name in enumerate(parts):
-            parts[name].append(e[j].elapsed_time(e[j + 1]))
-    avg = {n: sum(v) / len(v) for n, v in parts.items()}
+    avg = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
 
+    # Algorithmic work per launch.  Attention counts 2d FLOPs per multiply-add over the
+    # visible (query, key) pairs: forward S and O (4d per pair); the dQ pass S, dP and dQ
+    # (6d); the dK/dV pass S, dP, dV and dK (8d).  The headline counts the backward as
+    # 10d per pair (S and dP once), so the two passes together do 14d of it.
+    pairs_x_heads = wl.flops_fwd() / (4.0 * wl.d)
     f_fwd = wl.flops_fwd()
     f_bwd = wl.flops_bwd()
     flops_step = f_fwd + f_bwd
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     rl_bytes = 2.0 * C * Nr * Hr * dr * 2
+    rows = wl.B * wl.N * wl.Hq
+    prep_bytes = 2.0 * rows * wl.d * 2 + rows * 4 + 2 * rows * 4  # o, dout read; lse read; lse2, D written
+
+    def mfma(flop, n):
+        return {"bound": "mfma", "achieved": flop / (avg[n] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "algorithmic": flop}
+
+    def hbm(nbytes, n):
+        return {"bound": "hbm", "achieved": nbytes / (avg[n] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "algorithmic": nbytes}
+
     roof = {
-        "attn_bwd": {"bound": "mfma", "achieved": f_bwd / (avg["attn_bwd"] * 1e-3) / 1e12,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"},
-        "attn_fwd": {"bound": "mfma", "achieved": f_fwd / (avg["attn_fwd"] * 1e-3) / 1e12,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"},
-        "relayout_s2h": {"bound": "hbm", "achieved": rl_bytes / (avg["relayout_s2h"] * 1e-3) / 1e9,
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s"},
-        "relayout_h2s": {"bound": "hbm", "achieved": rl_bytes / (avg["relayout_h2s"] * 1e-3) / 1e9,
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s"},
+        "relayout_s2h": hbm(rl_bytes, "relayout_s2h"),
+        "attn_fwd": mfma(f_fwd, "attn_fwd"),
+        "attn_bwd_prep": hbm(prep_bytes, "attn_bwd_prep"),
+        "attn_bwd_dq": mfma(6.0 * wl.d * pairs_x_heads, "attn_bwd_dq"),
+        "attn_bwd_dkdv": mfma(8.0 * wl.d * pairs_x_heads, "attn_bwd_dkdv"),
+        "relayout_h2s": hbm(rl_bytes, "relayout_h2s"),
     }
     for n, r in roof.items():
         r["frac"] = r["achieved"] / r["peak"]
         r["ms"] = avg[n]
         r["traffic"] = measured_traffic(n)
     dominant = max(avg, key=avg.get)
-    dom = dict(roof[dominant])
-    dom.pop("ms")
+    dom = {k2: roof[dominant][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     dom["kernel"] = dominant
+    dom["ms"] = avg[dominant]
 
+    attn_ms = avg["attn_fwd"] + avg["attn_bwd_prep"] + avg["attn_bwd_dq"] + avg["attn_bwd_dkdv"]
     out = {
         "metric": METRIC,
         "value": value,
@@ -216,7 +306,8 @@ def main() -> int:
                    "kv_heads": wl.Hkv, "head_dim": wl.d, "causal": True,
                    "relayout": {"shape": [C, Nr, Hr, dr], "P": P}, "parallelism": "sp4-rank-share"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "attn_fwd_bwd_tflops": flops_step / ((avg["attn_fwd"] + avg["attn_bwd"]) * 1e-3) / 1e12,
+        "attn_fwd_bwd_ms": attn_ms,
+        "attn_fwd_bwd_tflops": flops_step / (attn_ms * 1e-3) / 1e12,
         "tokens_per_s": wl.B * wl.N / (ms_per_step * 1e-3),
         "roofline": dom,
         "roofline_all": roof,

@@ -121,6 +121,31 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       int32_t dtype, void *stream);
 
 /*
+ * The three stages of ul_attn_bwd, for callers that schedule them themselves.
+ *
+ *   UL_BWD_PREP   D_i = dout_i . o_i and lse in base-2 units, written to the
+ *                 workspace (reads o, dout, lse);
+ *   UL_BWD_DQ     dq from q, k, v, dout and the workspace;
+ *   UL_BWD_DKDV   dk and dv from q, k, v, dout and the workspace.
+ *
+ * `stages` is a non-empty OR of these bits; the selected stages run in the
+ * order above on `stream`.  DQ and DKDV read the workspace that PREP wrote for
+ * the same inputs and sizes, and do not depend on each other: after PREP a
+ * caller may run them on two streams (ordering them after PREP with events)
+ * so that each fills the other's idle compute units.  Arguments, validation
+ * and errors are those of ul_attn_bwd (every pointer is checked, whichever
+ * stages run), plus UNSUPPORTED for an empty mask or unknown bits.
+ * ul_attn_bwd(...) is ul_attn_bwd_stages(UL_BWD_ALL, ...).
+ */
+enum { UL_BWD_PREP = 1, UL_BWD_DQ = 2, UL_BWD_DKDV = 4, UL_BWD_ALL = 7 };
+
+ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const void *v,
+                             const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                             void *dv, void *workspace, size_t workspace_bytes, int64_t B,
+                             int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             float softmax_scale, int32_t causal, int32_t dtype, void *stream);
+
+/*
  * Sequence-sharded -> head-sharded relayout (the first all-to-all of the
  * step, section "How Does Ulysses Sequence Parallelism Actually Work?": each
  * GPU takes a chunk of N/P tokens, then ends up with all positions but a

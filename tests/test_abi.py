@@ -30,8 +30,9 @@ def addr(i):
 
 def test_exports_every_declared_symbol(L):
     names = B.declared_functions()
-    assert set(names) == {"ul_attn_fwd", "ul_attn_bwd", "ul_attn_bwd_workspace_bytes",
-                          "ul_relayout_s2h", "ul_relayout_h2s", "ul_status_str"}
+    assert set(names) == {"ul_attn_fwd", "ul_attn_bwd", "ul_attn_bwd_stages",
+                          "ul_attn_bwd_workspace_bytes", "ul_relayout_s2h", "ul_relayout_h2s",
+                          "ul_status_str"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -68,7 +69,7 @@ def test_fwd_validation(L, kw, code):
     assert fwd(L, **kw) == code
 
 
-def bwd(L, ws_bytes=None, ws=None, **kw):
+def bwd(L, ws_bytes=None, ws=None, stages=None, **kw):
     p = dict(Bsz=1, N=256, Hq=8, Hkv=2, d=128, scale=0.088, causal=1, dtype=B.UL_BF16)
     p.update(kw)
     need = L.ul_attn_bwd_workspace_bytes(p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"], p["dtype"])
@@ -77,8 +78,11 @@ def bwd(L, ws_bytes=None, ws=None, **kw):
         if n in p:
             ptrs[i] = p.pop(n)
     ws = addr(9) if ws is None else ws
-    return L.ul_attn_bwd(*ptrs, ws, need if ws_bytes is None else ws_bytes, p["Bsz"], p["N"], p["Hq"],
-                         p["Hkv"], p["d"], p["scale"], p["causal"], p["dtype"], None)
+    args = (*ptrs, ws, need if ws_bytes is None else ws_bytes, p["Bsz"], p["N"], p["Hq"], p["Hkv"],
+            p["d"], p["scale"], p["causal"], p["dtype"], None)
+    if stages is None:
+        return L.ul_attn_bwd(*args)
+    return L.ul_attn_bwd_stages(stages, *args)
 
 
 def test_workspace_bytes(L):
@@ -99,6 +103,14 @@ def test_workspace_bytes(L):
 ])
 def test_bwd_validation(L, kw, code):
     assert bwd(L, **kw) == code
+    # every stage subset validates the same way
+    for stages in (B.UL_BWD_PREP, B.UL_BWD_DQ, B.UL_BWD_DKDV, B.UL_BWD_ALL):
+        assert bwd(L, stages=stages, **kw) == code
+
+
+@pytest.mark.parametrize("stages", [0, 8, 9, -1])
+def test_bwd_stage_mask_validation(L, stages):
+    assert bwd(L, stages=stages) == 4
 
 
 @pytest.mark.parametrize("fn", ["ul_relayout_s2h", "ul_relayout_h2s"])

@@ -393,6 +393,11 @@ def _mutated(monkeypatch, which):
             p, dp, ds = orig_pdd(qh_r, kg, vg, do_r, lse_r, D_r, rows, scale, causal)
             return p, dp, p * dp
         monkeypatch.setattr(OA, "_p_dp_ds", bad)
+    elif which == "transposed_p":
+        def bad(qh_r, kg, vg, do_r, lse_r, D_r, rows, scale, causal):
+            p, dp, ds = orig_pdd(qh_r, kg, vg, do_r, lse_r, D_r, rows, scale, causal)
+            return p.T, dp, ds  # square at this size: dV = P dO instead of P^T dO
+        monkeypatch.setattr(OA, "_p_dp_ds", bad)
     elif which == "group_mapping":
         monkeypatch.setattr(OA, "_group", lambda h, Hq, Hkv: h % Hkv)
     elif which == "mask_off_by_one":
@@ -405,7 +410,8 @@ def _mutated(monkeypatch, which):
     return orig_group
 
 
-@pytest.mark.parametrize("which", ["sign_of_D", "dropped_D", "group_mapping", "mask_off_by_one"])
+@pytest.mark.parametrize("which", ["sign_of_D", "dropped_D", "transposed_p", "group_mapping",
+                                   "mask_off_by_one"])
 def test_planted_mistakes_are_caught(monkeypatch, which):
     B, N, Hq, Hkv, d = 1, 64, 4, 2, 16
     q, k, v, do = _qkv(B, N, Hq, Hkv, d, 170)

@@ -19,6 +19,7 @@ LIB_PATH = PKG / "libulattn.so"
 HEADER = PKG.parent / "include" / "ul_attn.h"
 
 UL_F32, UL_BF16 = 0, 1
+UL_BWD_PREP, UL_BWD_DQ, UL_BWD_DKDV, UL_BWD_ALL = 1, 2, 4, 7
 STATUS = {0: "UL_OK", 1: "UL_ERR_NULL", 2: "UL_ERR_SHAPE", 3: "UL_ERR_DIVISIBILITY",
           4: "UL_ERR_UNSUPPORTED", 5: "UL_ERR_ALIGNMENT", 6: "UL_ERR_WORKSPACE",
           7: "UL_ERR_OVERLAP", 8: "UL_ERR_HIP"}
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.ul_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32,
                                   i32, f32, i32, i32, vp]
         L.ul_attn_bwd.restype = ctypes.c_int
+        L.ul_attn_bwd_stages.argtypes = [i32] + L.ul_attn_bwd.argtypes
+        L.ul_attn_bwd_stages.restype = ctypes.c_int
         for name in ("ul_relayout_s2h", "ul_relayout_h2s"):
             f = getattr(L, name)
             f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
@@ -121,8 +124,13 @@ def workspace_bytes(B, N, Hq, Hkv, d, dtype_code) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = True,
-             workspace=None, dq=None, dk=None, dv=None, stream=None):
-    """dq, dk, dv of L = <dout, attention(q, k, v)>."""
+             workspace=None, dq=None, dk=None, dv=None, stream=None, stages: int = UL_BWD_ALL):
+    """dq, dk, dv of L = <dout, attention(q, k, v)>.
+
+    `stages` selects a subset of the backward's stages (UL_BWD_PREP, UL_BWD_DQ,
+    UL_BWD_DKDV); the default runs all three.  A partial call needs the same
+    `workspace` a previous PREP stage filled.
+    """
     import torch
 
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
@@ -137,10 +145,13 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib().ul_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, N, Hq, Hkv,
-                           d, scale, int(causal), code, _stream(stream))
-    _check("ul_attn_bwd", st)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), B, N, Hq, Hkv, d, scale, int(causal),
+            code, _stream(stream))
+    if stages == UL_BWD_ALL:
+        _check("ul_attn_bwd", lib().ul_attn_bwd(*args))
+    else:
+        _check("ul_attn_bwd_stages", lib().ul_attn_bwd_stages(int(stages), *args))
     return dq, dk, dv
 
 

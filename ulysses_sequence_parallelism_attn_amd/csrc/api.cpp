@@ -152,15 +152,16 @@ size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv
     return ul::attn_bwd_workspace_bytes(s, dtype);
 }
 
-ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
-                      const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                      void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
-                      int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
-                      int32_t dtype, void *stream) {
+ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const void *v,
+                             const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                             void *dv, void *workspace, size_t workspace_bytes, int64_t B,
+                             int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return UL_ERR_NULL;
     AttnSizes sz;
     const ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
+    if (stages < 1 || (stages & ~UL_BWD_ALL) != 0) return UL_ERR_UNSUPPORTED;
     const AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
     const size_t need = ul::attn_bwd_workspace_bytes(s, dtype);
     if (!workspace || workspace_bytes < need) return UL_ERR_WORKSPACE;
@@ -183,8 +184,18 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
             static_cast<const float *>(q), static_cast<const float *>(k),
             static_cast<const float *>(v), static_cast<const float *>(o),
             static_cast<const float *>(dout), lse, static_cast<float *>(dq),
-            static_cast<float *>(dk), static_cast<float *>(dv), workspace, s, hs));
-    return from_hip(ul::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, s, hs));
+            static_cast<float *>(dk), static_cast<float *>(dv), workspace, s, stages, hs));
+    return from_hip(ul::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, s, stages, hs));
+}
+
+ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                      void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
+                      int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                      int32_t dtype, void *stream) {
+    return ul_attn_bwd_stages(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                              workspace_bytes, B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype,
+                              stream);
 }
 
 }  // extern "C"

@@ -781,12 +781,15 @@ static hipError_t allow_lds(KernelT kernel, size_t bytes) {
 
 hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                                void *ws, const AttnShape &s, hipStream_t stream) {
+                                void *ws, const AttnShape &s, int stages, hipStream_t stream) {
     const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
     float *lse2 = static_cast<float *>(ws);
     float *Dv = reinterpret_cast<float *>(static_cast<char *>(ws) + round256(rows * sizeof(float)));
-    hipError_t err = launch_pre(o, dout, lse, lse2, Dv, s, true, stream);
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
+    if (stages & UL_BWD_PREP) {
+        err = launch_pre(o, dout, lse, lse2, Dv, s, true, stream);
+        if (err != hipSuccess) return err;
+    }
 
     DqParams dp;
     dp.q = static_cast<const uint16_t *>(q);
@@ -833,33 +836,44 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     if (kv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
 
     if (s.d == 128) {
-        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<128>, DqTile<128>::kLds)) != hipSuccess) return err;
-        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<128>, DkvTile<128>::kLds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, dim3((uint32_t)dq_items), dim3(kQThreads),
-                           DqTile<128>::kLds, stream, dp);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, dim3((uint32_t)kv_items), dim3(kKvThreads),
-                           DkvTile<128>::kLds, stream, kp);
+        if (stages & UL_BWD_DQ) {
+            if ((err = allow_lds(attn_bwd_dq_bf16_kernel<128>, DqTile<128>::kLds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<128>, dim3((uint32_t)dq_items), dim3(kQThreads),
+                               DqTile<128>::kLds, stream, dp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if (stages & UL_BWD_DKDV) {
+            if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<128>, DkvTile<128>::kLds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, dim3((uint32_t)kv_items), dim3(kKvThreads),
+                               DkvTile<128>::kLds, stream, kp);
+        }
     } else {
-        if ((err = allow_lds(attn_bwd_dq_bf16_kernel<64>, DqTile<64>::kLds)) != hipSuccess) return err;
-        if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<64>, DkvTile<64>::kLds)) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, dim3((uint32_t)dq_items), dim3(kQThreads),
-                           DqTile<64>::kLds, stream, dp);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, dim3((uint32_t)kv_items), dim3(kKvThreads),
-                           DkvTile<64>::kLds, stream, kp);
+        if (stages & UL_BWD_DQ) {
+            if ((err = allow_lds(attn_bwd_dq_bf16_kernel<64>, DqTile<64>::kLds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, dim3((uint32_t)dq_items), dim3(kQThreads),
+                               DqTile<64>::kLds, stream, dp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if (stages & UL_BWD_DKDV) {
+            if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<64>, DkvTile<64>::kLds)) != hipSuccess) return err;
+            hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, dim3((uint32_t)kv_items), dim3(kKvThreads),
+                               DkvTile<64>::kLds, stream, kp);
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                                const float *dout, const float *lse, float *dq, float *dk,
-                               float *dv, void *ws, const AttnShape &s, hipStream_t stream) {
+                               float *dv, void *ws, const AttnShape &s, int stages, hipStream_t stream) {
     const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
     float *lse2 = static_cast<float *>(ws);
     float *Dv = reinterpret_cast<float *>(static_cast<char *>(ws) + round256(rows * sizeof(float)));
-    hipError_t err = launch_pre(o, dout, lse, lse2, Dv, s, false, stream);
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
+    if (stages & UL_BWD_PREP) {
+        err = launch_pre(o, dout, lse, lse2, Dv, s, false, stream);
+        if (err != hipSuccess) return err;
+    }
     BwdF32Params p{q, k, v, dout, lse, Dv, dq, dk, dv, s.N, (int32_t)s.B, s.Hq, s.Hkv,
                    s.scale, s.causal, 0};
     p.n_blk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
@@ -867,13 +881,19 @@ hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, c
     const int64_t kv_items = ((s.N + kF32KvKeys - 1) / kF32KvKeys) * p.B * p.Hkv;
     if (dq_items > 0x7fffffff || kv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (s.d == 128) {
-        hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<128>, dim3((uint32_t)dq_items), dim3(kF32Rows), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<128>, dim3((uint32_t)kv_items), dim3(kF32KvKeys), 0, stream, p);
+        if (stages & UL_BWD_DQ) {
+            hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<128>, dim3((uint32_t)dq_items), dim3(kF32Rows), 0, stream, p);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if (stages & UL_BWD_DKDV)
+            hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<128>, dim3((uint32_t)kv_items), dim3(kF32KvKeys), 0, stream, p);
     } else {
-        hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, dim3((uint32_t)dq_items), dim3(kF32Rows), 0, stream, p);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-        hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<64>, dim3((uint32_t)kv_items), dim3(kF32KvKeys), 0, stream, p);
+        if (stages & UL_BWD_DQ) {
+            hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, dim3((uint32_t)dq_items), dim3(kF32Rows), 0, stream, p);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+        }
+        if (stages & UL_BWD_DKDV)
+            hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<64>, dim3((uint32_t)kv_items), dim3(kF32KvKeys), 0, stream, p);
     }
     return hipGetLastError();
 }

@@ -56,9 +56,9 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
 size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t dtype);
 hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                                const float *dout, const float *lse, float *dq, float *dk,
-                               float *dv, void *ws, const AttnShape &s, hipStream_t stream);
+                               float *dv, void *ws, const AttnShape &s, int stages, hipStream_t stream);
 hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
-                                void *ws, const AttnShape &s, hipStream_t stream);
+                                void *ws, const AttnShape &s, int stages, hipStream_t stream);
 
 }  // namespace ul
