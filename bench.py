@@ -165,7 +165,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus}, WORLD_SIZE {world} requested); "
-              "the multi-GPU exchange is not part of this build.", file=sys.stderr)
+              "the multi-GPU exchange is not implemented here.", file=sys.stderr)
         return 2
 
     import numpy as np
