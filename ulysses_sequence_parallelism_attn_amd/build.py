@@ -25,7 +25,7 @@ SOURCES = ["api.cpp", "relayout.hip", "attn_fwd.hip", "attn_bwd.hip"]
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",

@@ -325,7 +325,8 @@ struct DkvTile {
     static constexpr int kStats = 2 * kQT * 4;          // lse2 then D, fp32
     static constexpr int kStage = 2 * kBytes + kStats;  // Q, dO, stats
     static constexpr int kPds = kKvPairs * 4 * 64 * 16; // P[2], dS[2] fragments per pair, per lane
-    static constexpr int kStages = 4;                   // in flight x2 / produced / consumed
+    static constexpr int kAhead = 4;                    // steps of loads in flight
+    static constexpr int kStages = kAhead + 2;          // + produced + consumed
     static constexpr int kPdsStages = 2;
     static constexpr int kPds0 = kStages * kStage;
     static constexpr int kLds = kPds0 + kPdsStages * kPds;
@@ -358,12 +359,13 @@ struct DkvOffs {
 };
 
 // Producer step on the Q/dO tile at `tile` (stage base): S, dP -> P, dS
-// fragments (masked per MASK) -> the P/dS block at `pdsb`.
-template <int D, bool MASK>
+// fragments -> the P/dS block at `pdsb`.  `masked` applies the causal diagonal
+// and the ragged ends (only the softmax block is duplicated for it).
+template <int D>
 __device__ __forceinline__ void dkdv_produce(const bf16x8 *kf, const bf16x8 *vf,
                                              const UL_LDS unsigned char *tile, UL_LDS unsigned char *pdsb,
-                                             const DkvOffs<D> &o, int kg, int r0, int key, int N,
-                                             int causal, float c) {
+                                             const DkvOffs<D> &o, int kg, bool masked, int r0, int key,
+                                             int N, int causal, float c) {
     using T = DkvTile<D>;
     constexpr int KK = D / 16;
     f32x16 s = zero16(), dp = zero16();
@@ -383,6 +385,7 @@ __device__ __forceinline__ void dkdv_produce(const bf16x8 *kf, const bf16x8 *vf,
     }
     // C register r of lane group kg holds query row ckey(r, kg): two runs of 8
     // consecutive rows (16*hh + 8*kg ..), so the row statistics load as float4s.
+    float pv[16], dsv[16];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const UL_LDS unsigned char *st = tile + o.stat + hh * 16 * 4;
@@ -390,22 +393,29 @@ __device__ __forceinline__ void dkdv_produce(const bf16x8 *kf, const bf16x8 *vf,
         const f32x4 l1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + 16);
         const f32x4 d0 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4);
         const f32x4 d1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4 + 16);
-        float pv[8], dsv[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = hh * 8 + q;
             const float lz = q < 4 ? l0[q] : l1[q - 4];
             const float dz = q < 4 ? d0[q] : d1[q - 4];
-            float pz = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
-            if constexpr (MASK) {
-                const int i = r0 + hh * 16 + kg * 8 + q;
-                if (i >= N || key >= N || (causal && key > i)) pz = 0.f;
-            }
-            pv[q] = pz;
-            dsv[q] = pz * (dp[r] - dz);
+            pv[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
+            dsv[r] = dp[r] - dz;
         }
-        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + hh * 64 * 16) = __builtin_bit_cast(u32x4, pack8(pv));
-        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + (2 + hh) * 64 * 16) = __builtin_bit_cast(u32x4, pack8(dsv));
+    }
+    if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = r0 + ckey(r, kg);
+            if (i >= N || key >= N || (causal && key > i)) pv[r] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        float ds8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ds8[q] = pv[hh * 8 + q] * dsv[hh * 8 + q];
+        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + hh * 64 * 16) = __builtin_bit_cast(u32x4, pack8(pv + hh * 8));
+        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + (2 + hh) * 64 * 16) = __builtin_bit_cast(u32x4, pack8(ds8));
     }
 }
 
@@ -461,71 +471,91 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     // Steps: 32-row tiles from the end of the sequence down to the causal
     // diagonal, the group's query heads innermost.  Every workgroup walks the
     // rows in the same order, so workgroups resident at the same time stream
-    // the same Q/dO tiles and share them through L2.
+    // the same Q/dO tiles and share them through L2.  A cursor (step, head
+    // within the group, first row) advances one step at a time.
     const int qt_first = p.causal ? kb0 / kQT : 0;
     const int nqt = (N + kQT - 1) / kQT;
     const int per_head = nqt - qt_first;
     const int nsteps = per_head * grp;
-    auto row0 = [&](int s) { return (nqt - 1 - s / grp) * kQT; };
-    auto head = [&](int s) { return g * grp + s % grp; };
+    struct Cur {
+        int s, hi, r0;
+    };
+    auto advance = [&](Cur &cu) {  // stays on the last step once there
+        if (cu.s + 1 < nsteps) {
+            ++cu.s;
+            if (++cu.hi == grp) {
+                cu.hi = 0;
+                cu.r0 -= kQT;
+            }
+        }
+    };
+    const Cur first{0, 0, (nqt - 1) * kQT};
     const float c = p.scale_log2;
     const DkvOffs<D> o(lane, pair);
 
-    // Direct loads of step s into LDS stage s % 4: the Q and dO tiles are
-    // split evenly over the 8 waves; wave 0 also fetches the 32 lse2 and D
-    // values (one dword per lane).
-    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvWaves;  // per step, waves 1..7
-    static_assert(2 * Tile::INSTR % kKvWaves == 0, "Q and dO tiles split evenly over the waves");
-    auto issue_step = [&](int s, UL_LDS unsigned char *base) {
-        const int h = head(s), r0 = row0(s);
-        const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
-        const uint16_t *db = p.dout + ((int64_t)b * N * p.Hq + h) * D;
+    // Direct loads of a step into its LDS stage: the Q and dO tiles are split
+    // evenly over the 8 waves (each wave's share lies in one of the two), and
+    // the last wave also fetches the 32 lse2 and D values, one dword per lane.
+    // Rows past N re-read row N-1 (masked by the producer).
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvWaves;  // per step; the last wave has one more
+    static_assert(2 * Tile::INSTR % kKvWaves == 0 && Tile::INSTR % kDmaPerWave == 0,
+                  "Q and dO tiles split evenly over the waves");
+    const bool loads_do = wave * kDmaPerWave >= Tile::INSTR;
+    const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
+    const uint16_t *tens = loads_do ? p.dout : p.q;
+    const int tile_lds = loads_do ? T::kBytes : 0;
+    const uint32_t row_bytes = (uint32_t)q_rs * 2;
+    int dma_row[kDmaPerWave];
+    uint32_t dma_gran[kDmaPerWave];
 #pragma unroll
-        for (int k = 0; k < kDmaPerWave; ++k) {
-            const int u = wave * kDmaPerWave + k;  // 0 .. 2*INSTR-1: Q tile first, then dO
-            if (u < Tile::INSTR)
-                Tile::issue(qb, q_rs, r0, N, base, u, lane);
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        dma_row[k] = Tile::row(u0 + k, lane);
+        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
+    }
+    const int64_t dv_delta = (const char *)p.Dv - (const char *)p.lse2;
+    const bool stats_wave = wave == kKvWaves - 1;
+    auto issue = [&](const Cur &cu, UL_LDS unsigned char *base) {
+        const int lim = N - 1 - cu.r0;  // last valid row within the tile
+        const int h = g * grp + cu.hi;
+        const uint16_t *tb = tens + (((int64_t)b * N + cu.r0) * p.Hq + h) * D;
+#pragma unroll
+        for (int k = 0; k < kDmaPerWave; ++k)
+            dma_b128(tb, (uint32_t)min(dma_row[k], lim) * row_bytes + dma_gran[k],
+                     base + tile_lds + (u0 + k) * 1024);
+        if (stats_wave) {
+            const char *sb = (const char *)(p.lse2 + ((int64_t)b * p.Hq + h) * N + cu.r0);
+            const int r = min(lane & (kQT - 1), lim);
+            // lanes 0..31 read lse2, lanes 32..63 read D (a fixed distance away)
+            if (lane < kQT)
+                dma_b32(sb, (uint32_t)r * 4, base + 2 * T::kBytes);
             else
-                Tile::issue(db, q_rs, r0, N, base + T::kBytes, u - Tile::INSTR, lane);
-        }
-        if (wave == 0) {
-            const int i = min(r0 + (lane & (kQT - 1)), N - 1);
-            const float *src = (lane < kQT ? p.lse2 : p.Dv) + ((int64_t)b * p.Hq + h) * N + i;
-            dma_b32(src, base + 2 * T::kBytes);
+                dma_b32(sb + dv_delta, (uint32_t)r * 4, base + 2 * T::kBytes);
         }
     };
-    // the pair's keys see at least one row of step s
-    auto visible = [&](int s) { return (!p.causal || jw0 <= row0(s) + kQT - 1) && jw0 < N; };
+    // the pair's keys see at least one row of a step starting at row r0
+    auto visible = [&](int r0) { return (!p.causal || jw0 <= r0 + kQT - 1) && jw0 < N; };
 
-    if (nsteps > 0) issue_step(0, lds + T::stage(0));
-    if (nsteps > 1) issue_step(1, lds + T::stage(1));
-    __builtin_amdgcn_s_waitcnt(0x70);  // vmcnt(0) lgkmcnt(0)
-    asm volatile("s_barrier" ::: "memory");
+    // Loads always run kAhead steps ahead (past the last step they re-read it
+    // into a free stage), so every wave has the same number in flight at each
+    // barrier: waiting for all but the newest (kAhead-1) steps' worth leaves
+    // the oldest one landed.
+    Cur iss = first;
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+        ((issue(iss, lds + T::stage(J)), advance(iss)), ...);
+    }(std::make_integer_sequence<int, T::kAhead>{});
+    wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
 
-    // Iteration i (LDS stage i % 4, unrolled by 4 so stages are immediates):
-    // issue step i+2, producers handle step i, consumers step i-1; the
-    // barrier at the end waits for step i+1 (older than step i+2's loads).
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
+    // Iteration i (LDS stage i % 6, unrolled by 6 so stages are immediates):
+    // issue step i+4, producers handle step i, consumers step i-1; the
+    // barrier at the end waits for step i+1, the oldest load still in flight.
     auto run = [&](auto body) {
-        int i = 0;
-        for (; i + 4 <= nsteps + 1; i += 4) {
-            body(i, S0{});
-            body(i + 1, S1{});
-            body(i + 2, S2{});
-            body(i + 3, S3{});
+        for (int i0 = 0; i0 <= nsteps; i0 += T::kStages) {
+            [&]<int... J>(std::integer_sequence<int, J...>) {
+                ((i0 + J <= nsteps ? body(i0 + J, std::integral_constant<int, J>{}) : void()), ...);
+            }(std::make_integer_sequence<int, T::kStages>{});
         }
-        if (i <= nsteps) body(i, S0{});
-        if (i + 1 <= nsteps) body(i + 1, S1{});
-        if (i + 2 <= nsteps) body(i + 2, S2{});
-    };
-    auto finish = [&](int i) {
-        if (i + 2 < nsteps)
-            wait_vm_barrier<kDmaPerWave>();
-        else
-            wait_vm_barrier<0>();
+        // no load may still be writing this workgroup's LDS when it exits
+        __builtin_amdgcn_s_waitcnt(0x70);
     };
 
     if (producer) {
@@ -546,21 +576,20 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         // stage loads, or a wait for a fragment would also wait for the
         // newest stage.
         __builtin_amdgcn_s_waitcnt(0x70);
+        Cur cmp = first;
         run([&](int i, auto stage) {
-            constexpr int ST = decltype(stage)::value, NN = (ST + 2) % 4, PD = ST % 2;
-            if (i + 2 < nsteps) issue_step(i + 2, lds + T::stage(NN));
-            if (i < nsteps && visible(i)) {
-                const int r0 = row0(i);
-                const bool full = (!p.causal || r0 >= kb0 + kKeysPerWg) && r0 + kQT <= N &&
-                                  kb0 + kKeysPerWg <= N;
-                if (full)
-                    dkdv_produce<D, false>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, r0, key,
-                                           N, p.causal, c);
-                else
-                    dkdv_produce<D, true>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, r0, key,
-                                          N, p.causal, c);
+            constexpr int ST = decltype(stage)::value, NN = (ST + T::kAhead) % T::kStages, PD = ST % 2;
+            issue(iss, lds + T::stage(NN));
+            advance(iss);
+            if (i < nsteps && visible(cmp.r0)) {
+                const int r0 = cmp.r0;
+                const bool masked = (p.causal && r0 < kb0 + kKeysPerWg) || r0 + kQT > N ||
+                                    kb0 + kKeysPerWg > N;
+                dkdv_produce<D>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, masked, r0, key, N,
+                                p.causal, c);
             }
-            finish(i);
+            advance(cmp);
+            wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
         });
         return;
     }
@@ -572,11 +601,17 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         dkacc[eb] = zero16();
         dvacc[eb] = zero16();
     }
+    Cur cmp = first;
     run([&](int i, auto stage) {
-        constexpr int ST = decltype(stage)::value, NN = (ST + 2) % 4, PV = (ST + 3) % 4, PD = (ST + 1) % 2;
-        if (i + 2 < nsteps) issue_step(i + 2, lds + T::stage(NN));
-        if (i >= 1 && visible(i - 1)) dkdv_consume<D>(dkacc, dvacc, lds + T::stage(PV), lds + T::pds(PD), o);
-        finish(i);
+        constexpr int ST = decltype(stage)::value, NN = (ST + T::kAhead) % T::kStages;
+        constexpr int PV = (ST + T::kStages - 1) % T::kStages, PD = (ST + 1) % 2;
+        issue(iss, lds + T::stage(NN));
+        advance(iss);
+        if (i >= 1) {
+            if (visible(cmp.r0)) dkdv_consume<D>(dkacc, dvacc, lds + T::stage(PV), lds + T::pds(PD), o);
+            advance(cmp);
+        }
+        wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
     });
 
     // dK = scale * acc, dV = acc (bf16); lane column = key, registers = head dim

@@ -255,33 +255,48 @@ __device__ __forceinline__ uint32_t lds_addr(const UL_LDS void *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-__device__ __forceinline__ void dma_b128(const void *gsrc, const UL_LDS void *ldst) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_addr(ldst)), "v"(gsrc)
-                 : "memory", "m0");
+// A pointer the whole wave agrees on, held in scalar registers.
+template <typename T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ void dma_b32(const void *gsrc, const UL_LDS void *ldst) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(lds_addr(ldst)), "v"(gsrc)
-                 : "memory", "m0");
+// Lane L copies 16 (or 4) bytes from gbase + voff to LDS at ldst + 16 L (4 L).
+// gbase and ldst are wave-uniform; M0 (the LDS base of the transfer) is saved
+// and restored around the instruction.
+__device__ __forceinline__ void dma_b128(const void *gbase, uint32_t voff, const UL_LDS void *ldst) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "s"(lds_addr(ldst)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
 }
 
+__device__ __forceinline__ void dma_b32(const void *gbase, uint32_t voff, const UL_LDS void *ldst) {
+    uint32_t save;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(save)
+                 : "s"(lds_addr(ldst)), "v"(voff), "s"(uniform_ptr(gbase))
+                 : "memory");
+}
+
+// Wave instruction u of a [ROWS][D] tile covers LDS bytes [1024u, 1024u + 1024)
+// of the swizzled layout: lane L fetches the granule the layout keeps at slot
+// 64u + L, i.e. row u*ROWS_PER_INSTR + L/GPR, granule (L % GPR) ^ swz(row).
 template <int D, int ROWS>
 struct DmaTile {
     static constexpr int ROWB = D * 2, GPR = D / 8;
     static constexpr int INSTR = ROWS * ROWB / 1024;     // wave instructions per tile
     static constexpr int ROWS_PER_INSTR = 1024 / ROWB;
     static_assert(ROWS * ROWB % 1024 == 0, "tile must be a whole number of KB");
-
-    __device__ static __forceinline__ void issue(const uint16_t *gbase, int64_t stride, int r0, int nrows,
-                                                 UL_LDS unsigned char *tile, int u, int lane) {
-        const int r = u * ROWS_PER_INSTR + lane / GPR;
-        const int g = (lane % GPR) ^ swz<D>(r);
-        const int rr = min(r0 + r, nrows - 1);
-        dma_b128(gbase + (int64_t)rr * stride + g * 8, tile + u * 1024);
+    __device__ static __forceinline__ int row(int u, int lane) { return u * ROWS_PER_INSTR + lane / GPR; }
+    __device__ static __forceinline__ uint32_t gran_bytes(int u, int lane) {
+        return (uint32_t)(((lane % GPR) ^ swz<D>(row(u, lane))) * 16);
     }
 };
 
