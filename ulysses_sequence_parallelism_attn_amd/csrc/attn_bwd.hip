@@ -807,13 +807,6 @@ static hipError_t launch_pre(const void *o, const void *dout, const float *lse, 
     return hipGetLastError();
 }
 
-template <typename KernelT>
-static hipError_t allow_lds(KernelT kernel, size_t bytes) {
-    if (bytes <= 64 * 1024) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
 hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
                                 void *ws, const AttnShape &s, int stages, hipStream_t stream) {

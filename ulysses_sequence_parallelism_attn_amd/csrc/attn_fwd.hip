@@ -11,27 +11,34 @@
 // accumulator), never materialising scores beyond one tile.
 //
 // bf16 path (gfx950 MFMA):
-//  * workgroup = 4 waves; a work item is (batch b, KV head g, a block of query
-//    positions); each wave owns 64 query rows of one query head.  When the
-//    GQA group has >= 4 query heads the 4 waves are 4 heads of the group at
-//    the same 64 positions, so every K/V tile staged in LDS serves 4 x 64 rows.
+//  * workgroup = 8 waves, two per SIMD; a work item is (batch b, KV head g,
+//    a block of query positions) and each wave owns 32 query rows of one
+//    query head.  When the GQA group has >= 4 query heads, waves w and w+4
+//    are heads w of the group at two consecutive 32-row blocks, so every K/V
+//    tile staged in LDS serves 4 heads x 64 rows.
 //  * per 64-key tile:  S^T = K Q^T  (A = K rows from LDS, B = Q^T fragments
 //    held in registers), so a lane owns one query row and the row max/sum
 //    are in-lane plus one cross-half exchange; P^T (bf16) feeds O^T += V^T P^T
-//    directly from registers (A = V^T from a transposed LDS tile).
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//    in flight while the current one is computed.
+//    directly from registers (A = V^T by transposed LDS reads).
+//  * the two waves of a SIMD run half a tile apart (waves 4-7 one barrier
+//    behind waves 0-3): while one issues its 32 MFMAs (PV of the previous
+//    tile, then S of this one) the other does the softmax VALU work of its
+//    own tile, and the barrier between the halves swaps the roles.
+//  * K/V tiles go straight from global memory into a 4-stage LDS ring
+//    (global_load_lds, no register staging), two tiles ahead of use, the
+//    loads spread between the MFMAs.
 //  * tiles entirely above a wave's causal diagonal are skipped; the running
 //    max is only raised when a tile's max exceeds it by more than 2^8, which
 //    keeps O and l exact (both use the same reference) and skips most
 //    rescales of the accumulator.
 //  * work items are issued longest-first (late query blocks first) for load
-//    balance across the 256 CUs; items sharing a KV head stay on one XCD.
+//    balance across the 256 CUs.
 //
 // fp32 path: one thread per query row, K/V tiles in LDS, fp32 FMA and
 // online softmax; it is the exactness path (max-abs 1e-5), not a fast one.
 
 #include <type_traits>
+#include <utility>
 
 #include "mfma_tile.h"
 #include "ul_internal.h"
@@ -65,9 +72,16 @@ struct FwdParams {
 
 template <int D>
 struct FwdTile {
-    static constexpr int kBytes = kKT * D * 2;  // one K or V tile
-    static constexpr int kStage = 2 * kBytes;   // K then V
-    static constexpr int kLds = 2 * kStage;     // double-buffered
+    static constexpr int kBytes = kKT * D * 2;          // one K or V tile
+    static constexpr int kStages = 4;                   // tiles t .. t+3 in LDS
+    // K tiles of the 4 stages first, then the V tiles: every offset from the
+    // start of either region stays below 64 KB, so stage and step offsets fit
+    // the immediate offset of an LDS read (the V region's base is folded into
+    // the per-lane V fragment offsets once).
+    static constexpr int kVBase = kStages * kBytes;
+    static constexpr int kLds = 2 * kStages * kBytes;   // 128 KB at D = 128
+    static_assert(kVBase <= 65536, "stage offsets must fit an LDS immediate");
+    __device__ static constexpr int k_stage(int st) { return st * kBytes; }
 };
 
 // Per-wave state carried across key tiles.
@@ -79,33 +93,81 @@ struct FwdAcc {
     float l;        // this lane's partial running sum (the other half holds the rest)
 };
 
-// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-// MASK applies the causal diagonal and the ragged end of the sequence.
-template <int D, bool MASK>
-__device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
-                                         const UL_LDS unsigned char *kt,
-                                         const UL_LDS unsigned char *vt, const FragOffs<D> &o,
-                                         int kg, int j0, int row, int N, int causal, float c) {
-    constexpr int KK = D / 16, EB = D / 32, HALF = 32 * D * 2;
-    // S^T: one k-step of fragments in flight ahead of the MFMAs that use them
-    // (the barrier stops the scheduler from hoisting every LDS read of the
-    // tile, which would not fit in the register budget of 2 waves per SIMD).
-    f32x16 s[2] = {zero16(), zero16()};
-    bf16x8 a0 = lds_frag(kt, o.rm[0]), a1 = lds_frag(kt + HALF, o.rm[0]);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (kk + 1 < KK) {
-            n0 = lds_frag(kt, o.rm[kk + 1]);
-            n1 = lds_frag(kt + HALF, o.rm[kk + 1]);
+constexpr int kAhead = 6;  // A fragments read ahead of their MFMA
+
+// The MFMA half of a tile as one stream of 32 MFMAs, each with one A
+// fragment from LDS:
+//   PV steps  O^T += V^T P^T of the previous tile (A = V^T by transposed reads
+//             of the V tile at `vstage`, B = its P^T fragments in `pf`),
+//             4 x EB steps;
+//   S steps   S^T = K Q^T of this tile (A = K rows of the K tile at `kstage`,
+//             B = the wave's Q^T fragments), alternating the 32-key halves.
+// Addresses are absolute: `o` holds the lane's offsets with the LDS base (and
+// for V the V region) already added, the stage offsets are constants.  The A
+// fragments are read kAhead steps before their MFMA, enough to cover the LDS
+// latency while the other wave of the SIMD is not issuing MFMAs; with PV the
+// first kAhead of them are already in `ring` (fwd_prefetch).  `side(k)`, k <
+// NSIDE, runs between MFMAs spread over the stream (the tile loads).  The
+// scheduling barriers keep this order, and the register budget, intact.
+template <int D, bool PV, bool S, int NSIDE, typename Side>
+__device__ __forceinline__ void fwd_gemm(FwdAcc<D> &acc, const bf16x8 (&pf)[4], f32x16 (&s)[2],
+                                         const bf16x8 *qf, bf16x8 (&ring)[kAhead], uint32_t vstage,
+                                         uint32_t kstage, const FragOffs<D> &o, Side &&side) {
+    constexpr int EB = D / 32, KK = D / 16, HALF = 32 * D * 2;
+    constexpr int NPV = PV ? 4 * EB : 0, NS = S ? 2 * KK : 0, NSTEP = NPV + NS;
+    constexpr int EVERY = NSIDE > 0 ? NSTEP / NSIDE : 1;
+    auto frag = [&](int st) -> bf16x8 {
+        if (st < NPV) {
+            const uint32_t at = vstage + (st / EB) * 16 * D * 2;
+            return lds_tr_frag_at(o.tr[st % EB][0] + at, o.tr[st % EB][1] + at);
         }
-        s[0] = mfma32x32x16(a0, qf[kk], s[0]);
-        s[1] = mfma32x32x16(a1, qf[kk], s[1]);
-        a0 = n0;
-        a1 = n1;
+        const int x = st - NPV;
+        return lds_frag_at(o.rm[x / 2] + kstage + (x % 2) * HALF);
+    };
+    if constexpr (S) {
+        s[0] = zero16();
+        s[1] = zero16();
+    }
+    if constexpr (!PV) {
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i)
+            if (i < NSTEP) ring[i] = frag(i);
+    }
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+        const bf16x8 a = ring[st % kAhead];
+        if (st + kAhead < NSTEP) ring[st % kAhead] = frag(st + kAhead);
+        if (st < NPV) {
+            const int kap = st / EB, eb = st % EB;
+            acc.o[eb] = mfma32x32x16(a, pf[kap], acc.o[eb]);
+        } else {
+            const int x = st - NPV, kk = x / 2, js = x % 2;
+            s[js] = mfma32x32x16(a, qf[kk], s[js]);
+        }
+        if constexpr (NSIDE > 0)
+            if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
 
+// The first kAhead A fragments of the PV steps for the V tile at `vstage`.
+template <int D>
+__device__ __forceinline__ void fwd_prefetch(bf16x8 (&ring)[kAhead], uint32_t vstage, const FragOffs<D> &o) {
+    constexpr int EB = D / 32;
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) {
+        const uint32_t at = vstage + (st / EB) * 16 * D * 2;
+        ring[st] = lds_tr_frag_at(o.tr[st % EB][0] + at, o.tr[st % EB][1] + at);
+    }
+}
+
+// Online softmax of one tile: new running max, rescale of O and l when it
+// moves, P = exp2(S c - m) packed to bf16 B fragments.  MASK applies the
+// causal diagonal and the ragged end of the sequence.
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_softmax(FwdAcc<D> &acc, f32x16 (&s)[2], bf16x8 (&pf)[4], int kg, int j0,
+                                            int row, int N, int causal, float c) {
+    constexpr int EB = D / 32;
     float mx = -INFINITY;
 #pragma unroll
     for (int js = 0; js < 2; ++js)
@@ -121,7 +183,7 @@ __device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
 
     // Raise the running max only when the tile exceeds it by 2^8: O and l
     // share the reference, so the result is exact either way.
-    const bool raise = tmax > acc.m + 8.0f;
+    const bool raise = tmax > acc.m + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise)) {
         const float mnew = raise ? tmax : acc.m;
         const float alpha = acc.m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(acc.m - mnew);
@@ -133,7 +195,6 @@ __device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
         acc.m = mnew;
     }
 
-    bf16x8 pf[4];
     float ls = 0.f;
 #pragma unroll
     for (int js = 0; js < 2; ++js)
@@ -148,21 +209,18 @@ __device__ __forceinline__ void fwd_tile(FwdAcc<D> &acc, const bf16x8 *qf,
             pf[js * 2 + hh] = pack8(e);
         }
     acc.l += ls;
-
-    // O^T += V^T P^T, same one-step lookahead
-    bf16x8 va = lds_tr_frag(vt, o.tr[0][0], o.tr[0][1]);
+    // Pin P and l here: otherwise the compiler sinks the exponentials to their
+    // use, into the next MFMA half, which is the other wave's softmax time.
 #pragma unroll
-    for (int step = 0; step < 4 * EB; ++step) {
-        const int kap = step / EB, eb = step % EB;
-        bf16x8 vn = va;
-        if (step + 1 < 4 * EB) {
-            const int nk = (step + 1) / EB, ne = (step + 1) % EB;
-            vn = lds_tr_frag(vt + nk * 16 * D * 2, o.tr[ne][0], o.tr[ne][1]);
-        }
-        acc.o[eb] = mfma32x32x16(va, pf[kap], acc.o[eb]);
-        va = vn;
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pf[i]));
+    asm volatile("" : "+v"(acc.l));
+}
+
+// A workgroup barrier that the scheduler does not move work across.
+__device__ __forceinline__ void fence_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>
@@ -170,9 +228,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
     using T = FwdTile<D>;
+    using Tile = DmaTile<D, kKT>;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
 
     // ---- work item, longest first: item = rank * (B*Hkv*head_groups) + rest
@@ -195,8 +254,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
 
     const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
     const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
-    const uint16_t *kb = p.k + ((int64_t)b * N * p.Hkv + g) * D;
-    const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
 
     // ---- Q^T fragments (B operand: column = query row, k = head dim)
     constexpr int KK = D / 16, EB = D / 32;
@@ -205,6 +262,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     for (int kk = 0; kk < KK; ++kk)
         qf[kk] = as_bf16x8(row < N ? *reinterpret_cast<const u32x4 *>(qb + row * q_rs + kk * 16 + kg * 8)
                                    : u32x4{0, 0, 0, 0});
+    // Retire these loads: inside the loop vmcnt counts only the tile loads.
+    __builtin_amdgcn_s_waitcnt(0x70);
 
     FwdAcc<D> acc;
 #pragma unroll
@@ -217,59 +276,135 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const int ntiles = (kend + kKT - 1) / kKT;
     const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
     const float c = p.scale_log2;
-    const FragOffs<D> fo(lane);
+    // Absolute LDS addresses: the lane's fragment offsets plus the LDS base
+    // (and, for V, the V region); the empty asm keeps the compiler from
+    // splitting the sums again into out-of-range immediates.
+    FragOffs<D> fo(lane);
+    {
+        const uint32_t base = (uint32_t)(uintptr_t)lds;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            fo.rm[kk] += base;
+            asm volatile("" : "+v"(fo.rm[kk]));
+        }
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                fo.tr[e][x] += base + T::kVBase;
+                asm volatile("" : "+v"(fo.tr[e][x]));
+            }
+    }
 
-    TileStage<D, kKT, kThreads> sk, sv;
-    sk.load(kb, kv_rs, 0, N, tid);
-    sv.load(vb, kv_rs, 0, N, tid);
-    sk.store(lds, tid);
-    sv.store(lds + T::kBytes, tid);
-    __syncthreads();
-
-    // One pipeline step: fetch tile t+1 into registers, compute tile t from
-    // LDS, park tile t+1 in the other LDS stage.  The unmasked and masked
-    // tiles run in separate loops so each loop keeps only its own invariants.
-    auto step = [&](int t, auto masked, auto stage) {
-        constexpr int st = decltype(stage)::value;
+    // Direct loads of tile t into its LDS stage: the K and V tiles are split
+    // evenly over the 8 waves, each wave's share inside one of the two.  Keys
+    // past N re-read key N-1 (their scores are masked, so P is 0 there).
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kWaves;
+    static_assert(2 * Tile::INSTR % kWaves == 0 && Tile::INSTR % kDmaPerWave == 0,
+                  "K and V tiles split evenly over the waves");
+    const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
+    const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + ((int64_t)b * N * p.Hkv + g) * D;
+    const int tile_lds = loads_v ? T::kVBase : 0;
+    const uint32_t row_bytes = (uint32_t)kv_rs * 2;
+    uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
+        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
+    }
+    // load k of this wave's share of tile t into the stage at `base`
+    auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
         const int j0 = t * kKT;
-        if (t + 1 < ntiles) {
-            sk.load(kb, kv_rs, j0 + kKT, N, tid);
-            sv.load(vb, kv_rs, j0 + kKT, N, tid);
-        }
-        const UL_LDS unsigned char *kt = lds + st * T::kStage;
-        const UL_LDS unsigned char *vt = kt + T::kBytes;
-        if constexpr (decltype(masked)::value) {
-            if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
-                fwd_tile<D, true>(acc, qf, kt, vt, fo, kg, j0, row, N, p.causal, c);
-        } else {
-            fwd_tile<D, false>(acc, qf, kt, vt, fo, kg, j0, row, N, p.causal, c);
-        }
-        if (t + 1 < ntiles) {
-            UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;
-            sk.store(nk, tid);
-            sv.store(nk + T::kBytes, tid);
-        }
-        __syncthreads();
+        const uint32_t lim = (uint32_t)(N - 1 - j0) * row_bytes;  // last key of the sequence
+        dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
+                 base + tile_lds + (u0 + k) * 1024);
     };
-    // Tiles go in pairs so that the LDS stage is a compile-time offset.
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    int t = 0;
-    for (; t + 1 < n_full; t += 2) {
-        step(t, std::false_type{}, S0{});
-        step(t + 1, std::false_type{}, S1{});
+    auto issue = [&](int t, UL_LDS unsigned char *base) {
+#pragma unroll
+        for (int k = 0; k < kDmaPerWave; ++k) issue_k(t, k, base);
+    };
+    // tile t holds keys this wave's rows can see
+    auto visible = [&](int t) { return !p.causal || t * kKT <= i0 + kRowsPerWave - 1; };
+
+    // Two groups of 4 waves, one wave of each per SIMD, run half a tile apart:
+    // while one wave of a SIMD issues its MFMAs (PV of tile t-1, S of tile t)
+    // the other runs the softmax VALU work of its own tile, and the barrier
+    // between the halves swaps the roles.  Both groups run the same sequence
+    // of (MFMA half, barrier, softmax half, barrier) per tile; the second group
+    // enters it one barrier later and the first leaves it with one extra
+    // barrier, so every wave meets the same number of barriers.
+    //
+    // Tile t sits in stage t % 4 from its load (issued at the start of the MFMA
+    // half of tile t-2) to the second group's PV of it (the MFMA half of tile
+    // t+1); each wave waits for its share of tile t+1 before the barrier that
+    // ends its MFMA half of tile t, which is before anyone reads it.
+    const bool lagging = wave >= kWaves / 2;
+    issue(0, lds + T::k_stage(0));
+    if (ntiles > 1) {
+        issue(1, lds + T::k_stage(1));
+        wait_vm_barrier<kDmaPerWave>();
+    } else {
+        wait_vm_barrier<0>();
     }
-    if (t < n_full) {
-        step(t, std::false_type{}, S0{});
-        ++t;
-        if (t < ntiles) step(t, std::true_type{}, S1{});
-        ++t;
+    if (lagging) fence_barrier();
+
+    f32x16 s[2];
+    bf16x8 pf[4];
+    bf16x8 ring[kAhead];
+    // One tile: the MFMA half (PV of tile t-1, S of tile t, the loads of tile
+    // t+2 between the MFMAs), then the softmax half, which ends by reading the
+    // first V fragments of the next MFMA half.  `stage(x)` is tile x's stage
+    // offset.  FULL: both tiles take part and tile t is unmasked (the steady
+    // state, one straight block); otherwise each part is checked on its own.
+    auto body = [&](int t, auto full, auto stage) {
+        constexpr bool FULL = decltype(full)::value;
+        const bool more = t + 2 < ntiles;
+        UL_LDS unsigned char *nx = lds + stage(t + 2);
+        if constexpr (FULL) {
+            fwd_gemm<D, true, true, kDmaPerWave>(acc, pf, s, qf, ring, stage(t - 1), stage(t), fo,
+                                                 [&](int k) {
+                                                     if (more) issue_k(t + 2, k, nx);
+                                                 });
+        } else {
+            if (more) issue(t + 2, nx);
+            auto none = [](int) {};
+            if (t >= 1 && visible(t - 1))
+                fwd_gemm<D, true, false, 0>(acc, pf, s, qf, ring, stage(t - 1), 0, fo, none);
+            if (t < ntiles && visible(t)) fwd_gemm<D, false, true, 0>(acc, pf, s, qf, ring, 0, stage(t), fo, none);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more)
+            wait_vm_barrier<kDmaPerWave>();
+        else
+            wait_vm_barrier<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (FULL || (t < ntiles && visible(t))) {
+            if constexpr (FULL)
+                fwd_softmax<D, false>(acc, s, pf, kg, t * kKT, row, N, p.causal, c);
+            else
+                fwd_softmax<D, true>(acc, s, pf, kg, t * kKT, row, N, p.causal, c);
+            fwd_prefetch<D>(ring, stage(t), fo);
+        }
+        fence_barrier();
+    };
+    // Tile 0 (no PV yet), then the whole unmasked tiles 1 .. n_full-1 in
+    // fours so that every stage offset is a constant, then the rest (at most
+    // three unmasked tiles, the masked ones and the last PV) with computed
+    // stages and the masking softmax, which is exact on unmasked tiles too.
+    auto rt_stage = [](int x) { return (uint32_t)T::k_stage(x & (T::kStages - 1)); };
+    body(0, std::false_type{}, rt_stage);
+    int t0 = 1;
+    for (; t0 + T::kStages <= n_full; t0 += T::kStages) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            // x - t0 + 1 folds to a constant for every tile index body derives from t0 + J
+            (body(t0 + J, std::true_type{},
+                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+             ...);
+        }(std::make_integer_sequence<int, T::kStages>{});
     }
-    for (; t + 1 < ntiles; t += 2) {
-        step(t, std::true_type{}, S0{});
-        step(t + 1, std::true_type{}, S1{});
-    }
-    if (t < ntiles) step(t, std::true_type{}, S0{});
+    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage);
+    if (!lagging) fence_barrier();
 
     // ---- epilogue: normalise, round to bf16, write O and lse
     const float ltot = half_sum(acc.l);
@@ -394,10 +529,14 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)items), block(kThreads);
-    if (s.d == 128)
+    hipError_t err;
+    if (s.d == 128) {
+        if ((err = allow_lds(attn_fwd_bf16_kernel<128>, FwdTile<128>::kLds)) != hipSuccess) return err;
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, FwdTile<128>::kLds, stream, p);
-    else
+    } else {
+        if ((err = allow_lds(attn_fwd_bf16_kernel<64>, FwdTile<64>::kLds)) != hipSuccess) return err;
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, FwdTile<64>::kLds, stream, p);
+    }
     return hipGetLastError();
 }
 

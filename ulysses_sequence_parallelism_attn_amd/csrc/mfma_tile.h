@@ -180,6 +180,21 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const UL_LDS unsigned char *base, 
     return r;
 }
 
+// The same reads at absolute LDS byte addresses (a per-lane register plus a
+// compile-time offset, which the ds_read takes as its immediate).
+__device__ __forceinline__ bf16x8 lds_frag_at(uint32_t addr) {
+    return as_bf16x8(*reinterpret_cast<const UL_LDS u32x4 *>((uintptr_t)addr));
+}
+
+__device__ __forceinline__ bf16x8 lds_tr_frag_at(uint32_t lo_addr, uint32_t hi_addr) {
+    const v4bf16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((UL_LDS v4bf16 *)(uintptr_t)lo_addr);
+    const v4bf16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((UL_LDS v4bf16 *)(uintptr_t)hi_addr);
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
 // Offsets of the two fragment kinds every attention kernel reads from a
 // [rows][D] tile: row fragments of row kperm(m) (+ multiples of 32 rows) for
 // k-step kk, and transposed fragments for column block eb (+ multiples of 16

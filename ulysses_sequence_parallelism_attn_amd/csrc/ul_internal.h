@@ -34,6 +34,14 @@ struct FastDiv32 {
     }
 };
 
+// Lets `kernel` take `bytes` of dynamic LDS (the default limit is 64 KB).
+template <typename KernelT>
+inline hipError_t allow_lds(KernelT kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; arguments are already
 // validated by the host API.
