@@ -26,6 +26,7 @@
 // exactness path).
 
 #include <type_traits>
+#include <utility>
 
 #include "mfma_tile.h"
 #include "ul_internal.h"
@@ -82,17 +83,26 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
 //
 // Geometry as the forward: 8 waves (2 per SIMD), 32 query rows per wave; the
 // waves of a workgroup are the GQA group's query heads at the same positions,
-// so each K/V tile staged in LDS serves all of them.  Per 64-key tile and
-// 32-key half js:
+// so each K/V tile staged in LDS serves all of them.  Per 32-key tile:
 //   S^T  = K Q^T       (A = K rows, B = Q^T fragments in registers)
 //   dP^T = V dO^T      (A = V rows, B = dO^T fragments in registers)
 //   dS^T = P^T (dP^T - D),  P^T = exp2(S^T c - lse2)
-//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads, B = dS^T from C)
+//   dQ^T += K^T dS^T   (A = K^T by transposed LDS reads, B = dS^T fragments)
+// As in the forward, the two waves of a SIMD run half a tile apart: one
+// issues the 24 MFMAs of its tile (dQ of the previous tile, then S and dP of
+// this one) while the other forms dS.  K/V tiles go straight from global
+// memory into an 8-stage LDS ring, 6 tiles ahead of use.  (32-key tiles keep
+// S and dP of a tile, the dQ accumulator and the Q^T / dO^T fragments within
+// the 256 registers of a wave at 2 waves per SIMD.)
 
 constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kKT = 64;
+constexpr int kDqKT = 32;   // keys per tile
+// A fragments read ahead of their MFMA: 6, but no more than the dQ steps of
+// a tile, since the prefetch at the end of the softmax half covers only those.
+template <int D>
+constexpr int kQAhead = 2 * (D / 32) < 6 ? 2 * (D / 32) : 6;
 
 struct DqParams {
     const uint16_t *q, *k, *v, *dout;
@@ -106,66 +116,112 @@ struct DqParams {
 
 template <int D>
 struct DqTile {
-    static constexpr int kBytes = kKT * D * 2;
-    static constexpr int kStage = 2 * kBytes;  // K then V
-    static constexpr int kLds = 2 * kStage;
+    static constexpr int kBytes = kDqKT * D * 2;      // one K or V tile
+    static constexpr int kStages = 8;                 // LDS ring of tiles
+    static constexpr int kAhead = kStages - 2;        // tiles loaded ahead of use
+    // K tiles of every stage, then the V tiles: offsets from the start of
+    // either region stay below 64 KB and fit an LDS read's immediate.
+    static constexpr int kVBase = kStages * kBytes;
+    static constexpr int kLds = 2 * kStages * kBytes;  // 128 KB at D = 128
+    static_assert(kVBase <= 65536, "stage offsets must fit an LDS immediate");
+    __device__ static constexpr int k_stage(int st) { return st * kBytes; }
 };
 
-template <int D, bool MASK>
-__device__ __forceinline__ void dq_tile(f32x16 *dqacc, const bf16x8 *qf, const bf16x8 *dof,
-                                        float lse2, float Drow, const UL_LDS unsigned char *kt,
-                                        const UL_LDS unsigned char *vt, const FragOffs<D> &o,
-                                        int kg, int j0, int row, int N, int causal, float c) {
-    constexpr int KK = D / 16, EB = D / 32, ROWB = D * 2;
-#pragma unroll
-    for (int js = 0; js < 2; ++js) {
-        const UL_LDS unsigned char *kj = kt + js * 32 * ROWB, *vj = vt + js * 32 * ROWB;
-        f32x16 s = zero16(), dp = zero16();
-        bf16x8 ak = lds_frag(kj, o.rm[0]), av = lds_frag(vj, o.rm[0]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            bf16x8 nk = ak, nv = av;
-            if (kk + 1 < KK) {
-                nk = lds_frag(kj, o.rm[kk + 1]);
-                nv = lds_frag(vj, o.rm[kk + 1]);
-            }
-            s = mfma32x32x16(ak, qf[kk], s);
-            dp = mfma32x32x16(av, dof[kk], dp);
-            ak = nk;
-            av = nv;
-            __builtin_amdgcn_sched_barrier(0);
+// Absolute LDS addresses of this lane's fragments: K and V rows for S and dP,
+// K^T halves for dQ (the LDS base and the V region already added).
+template <int D>
+struct DqOffs {
+    static constexpr int KK = D / 16, EB = D / 32;
+    uint32_t k[KK], v[KK], tr[EB][2];
+};
+
+// The MFMA half of a tile as one stream of A fragments from LDS:
+//   DQ steps   dQ^T += K^T dS^T of the previous tile (its K tile at `pstage`,
+//              B = its two dS^T fragments), 2 x EB steps;
+//   SDP steps  S^T = K Q^T and dP^T = V dO^T of this tile (tiles at
+//              `cstage`), alternating per k-step.
+// With DQ the first kQAhead<D> fragments are already in `ring` (dq_prefetch).
+// `side(k)`, k < NSIDE, runs between MFMAs spread over the stream.
+template <int D, bool DQ, bool SDP, int NSIDE, typename Side>
+__device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f32x16 &s, f32x16 &dp,
+                                        const bf16x8 *qf, const bf16x8 *dof, bf16x8 (&ring)[kQAhead<D>],
+                                        uint32_t pstage, uint32_t cstage, const DqOffs<D> &o, Side &&side) {
+    constexpr int EB = D / 32, KK = D / 16;
+    constexpr int NDQ = DQ ? 2 * EB : 0, NSD = SDP ? 2 * KK : 0, NSTEP = NDQ + NSD;
+    static_assert(!DQ || NDQ >= kQAhead<D>, "the prefetched ring holds dQ steps only");
+    constexpr int EVERY = NSIDE > 0 ? NSTEP / NSIDE : 1;
+    auto frag = [&](int st) -> bf16x8 {
+        if (st < NDQ) {
+            const uint32_t at = pstage + (st / EB) * 16 * D * 2;
+            return lds_tr_frag_at(o.tr[st % EB][0] + at, o.tr[st % EB][1] + at);
         }
-        bf16x8 dsf[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            float ds[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int r = hh * 8 + q;
-                float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-                if constexpr (MASK) {
-                    const int j = j0 + js * 32 + ckey(r, kg);
-                    if (j >= N || (causal && j > row)) pv = 0.f;
-                }
-                ds[q] = pv * (dp[r] - Drow);
-            }
-            dsf[hh] = pack8(ds);
-        }
-        // dQ^T += K^T dS^T over this half's 32 keys (2 k-steps of 16)
-        bf16x8 a = lds_tr_frag(kj, o.tr[0][0], o.tr[0][1]);
-#pragma unroll
-        for (int st = 0; st < 2 * EB; ++st) {
-            const int hh = st / EB, eb = st % EB;
-            bf16x8 n = a;
-            if (st + 1 < 2 * EB) {
-                const int nh = (st + 1) / EB, ne = (st + 1) % EB;
-                n = lds_tr_frag(kj + nh * 16 * ROWB, o.tr[ne][0], o.tr[ne][1]);
-            }
-            dqacc[eb] = mfma32x32x16(a, dsf[hh], dqacc[eb]);
-            a = n;
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        const int x = st - NDQ, kk = x / 2;
+        return lds_frag_at((x % 2 == 0 ? o.k[kk] : o.v[kk]) + cstage);
+    };
+    if constexpr (SDP) {
+        s = zero16();
+        dp = zero16();
     }
+    if constexpr (!DQ) {
+#pragma unroll
+        for (int i = 0; i < kQAhead<D>; ++i)
+            if (i < NSTEP) ring[i] = frag(i);
+    }
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+        const bf16x8 a = ring[st % kQAhead<D>];
+        if (st + kQAhead<D> < NSTEP) ring[st % kQAhead<D>] = frag(st + kQAhead<D>);
+        if (st < NDQ) {
+            const int kap = st / EB, eb = st % EB;
+            dqacc[eb] = mfma32x32x16(a, dsf[kap], dqacc[eb]);
+        } else {
+            const int x = st - NDQ, kk = x / 2;
+            if (x % 2 == 0)
+                s = mfma32x32x16(a, qf[kk], s);
+            else
+                dp = mfma32x32x16(a, dof[kk], dp);
+        }
+        if constexpr (NSIDE > 0)
+            if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The first kQAhead<D> A fragments of the DQ steps for the K tile at `stage`.
+template <int D>
+__device__ __forceinline__ void dq_prefetch(bf16x8 (&ring)[kQAhead<D>], uint32_t stage, const DqOffs<D> &o) {
+    constexpr int EB = D / 32;
+#pragma unroll
+    for (int st = 0; st < kQAhead<D>; ++st) {
+        const uint32_t at = stage + (st / EB) * 16 * D * 2;
+        ring[st] = lds_tr_frag_at(o.tr[st % EB][0] + at, o.tr[st % EB][1] + at);
+    }
+}
+
+// dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2), as two bf16 B
+// fragments of 16 keys.  MASK zeroes P past the causal diagonal and the
+// ragged end.
+template <bool MASK>
+__device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f32x16 &dp, float lse2, float Drow,
+                                      int kg, int j0, int row, int N, int causal, float c) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        float ds[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int r = hh * 8 + q;
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+            if constexpr (MASK) {
+                const int j = j0 + ckey(r, kg);
+                if (j >= N || (causal && j > row)) pv = 0.f;
+            }
+            ds[q] = pv * (dp[r] - Drow);
+        }
+        dsf[hh] = pack8(ds);
+    }
+    // keep the exponentials here rather than sunk into the next MFMA half
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(dsf[i]));
 }
 
 template <int D>
@@ -173,8 +229,9 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     extern __shared__ __align__(16) unsigned char smem_raw[];
     UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
     using T = DqTile<D>;
+    using Tile = DmaTile<D, kDqKT>;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
 
     const int per_rank = p.B * p.Hkv * p.head_groups;
@@ -195,8 +252,6 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
     const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
     const uint16_t *dob = p.dout + ((int64_t)b * N * p.Hq + h) * D;
-    const uint16_t *kb = p.k + ((int64_t)b * N * p.Hkv + g) * D;
-    const uint16_t *vb = p.v + ((int64_t)b * N * p.Hkv + g) * D;
 
     constexpr int KK = D / 16, EB = D / 32;
     bf16x8 qf[KK], dof[KK];
@@ -211,64 +266,131 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const int64_t so = ((int64_t)b * p.Hq + h) * N + (ok ? row : 0);
     const float lse2 = ok ? p.lse2[so] : 0.f;
     const float Drow = ok ? p.Dv[so] : 0.f;
+    // Retire these loads: inside the loop vmcnt counts only the tile loads.
+    __builtin_amdgcn_s_waitcnt(0x70);
 
     f32x16 dqacc[EB];
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) dqacc[eb] = zero16();
 
     const int kend = p.causal ? min(N, wg_pos0 + wg_rows) : N;
-    const int ntiles = (kend + kKT - 1) / kKT;
-    const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
+    const int ntiles = (kend + kDqKT - 1) / kDqKT;
+    const int n_full = p.causal ? min(wg_pos0, N) / kDqKT : N / kDqKT;
     const float c = p.scale_log2;
-    const FragOffs<D> fo(lane);
 
-    TileStage<D, kKT, kQThreads> sk, sv;
-    sk.load(kb, kv_rs, 0, N, tid);
-    sv.load(vb, kv_rs, 0, N, tid);
-    sk.store(lds, tid);
-    sv.store(lds + T::kBytes, tid);
-    __syncthreads();
+    // Absolute LDS addresses; the empty asm keeps the compiler from splitting
+    // the sums again into out-of-range immediates.
+    DqOffs<D> fo;
+    {
+        const FragOffs<D> f(lane);
+        const uint32_t base = (uint32_t)(uintptr_t)lds;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            fo.k[kk] = f.rm[kk] + base;
+            fo.v[kk] = f.rm[kk] + base + T::kVBase;
+            asm volatile("" : "+v"(fo.k[kk]));
+            asm volatile("" : "+v"(fo.v[kk]));
+        }
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                fo.tr[e][x] = f.tr[e][x] + base;
+                asm volatile("" : "+v"(fo.tr[e][x]));
+            }
+    }
 
-    auto step = [&](int t, auto masked, auto stage) {
-        constexpr int st = decltype(stage)::value;
-        const int j0 = t * kKT;
-        if (t + 1 < ntiles) {
-            sk.load(kb, kv_rs, j0 + kKT, N, tid);
-            sv.load(vb, kv_rs, j0 + kKT, N, tid);
-        }
-        const UL_LDS unsigned char *kt = lds + st * T::kStage;
-        const UL_LDS unsigned char *vt = kt + T::kBytes;
-        if constexpr (decltype(masked)::value) {
-            if (!p.causal || j0 <= i0 + kRowsPerWave - 1)
-                dq_tile<D, true>(dqacc, qf, dof, lse2, Drow, kt, vt, fo, kg, j0, row, N, p.causal, c);
-        } else {
-            dq_tile<D, false>(dqacc, qf, dof, lse2, Drow, kt, vt, fo, kg, j0, row, N, p.causal, c);
-        }
-        if (t + 1 < ntiles) {
-            UL_LDS unsigned char *nk = lds + (st ^ 1) * T::kStage;
-            sk.store(nk, tid);
-            sv.store(nk + T::kBytes, tid);
-        }
-        __syncthreads();
+    // Direct loads of tile t into its LDS stage: the K and V tiles are split
+    // evenly over the 8 waves.  Keys past N re-read key N-1 (their P is 0).
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kQWaves;
+    static_assert(2 * Tile::INSTR % kQWaves == 0 && Tile::INSTR % kDmaPerWave == 0,
+                  "K and V tiles split evenly over the waves");
+    static_assert((T::kAhead - 1) * kDmaPerWave < 16, "vmcnt immediate");
+    const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
+    const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + ((int64_t)b * N * p.Hkv + g) * D;
+    const int tile_lds = loads_v ? T::kVBase : 0;
+    const uint32_t row_bytes = (uint32_t)kv_rs * 2;
+    uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
+        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
+    }
+    auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
+        const int j0 = t * kDqKT;
+        const uint32_t lim = (uint32_t)(N - 1 - j0) * row_bytes;
+        dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
+                 base + tile_lds + (u0 + k) * 1024);
     };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    int t = 0;
-    for (; t + 1 < n_full; t += 2) {
-        step(t, std::false_type{}, S0{});
-        step(t + 1, std::false_type{}, S1{});
+    auto issue = [&](int t, UL_LDS unsigned char *base) {
+#pragma unroll
+        for (int k = 0; k < kDmaPerWave; ++k) issue_k(t, k, base);
+    };
+    auto visible = [&](int t) { return !p.causal || t * kDqKT <= i0 + kRowsPerWave - 1; };
+
+    // The forward's schedule with a deeper ring: waves 4-7 run one barrier
+    // behind waves 0-3; tile t sits in stage t % 8 from its load (in the MFMA
+    // half of tile t-6) to the lagging group's dQ of it (MFMA half of tile
+    // t+1); each wave waits for its share of tile t+1 before the barrier
+    // ending its MFMA half of tile t (all but the 5 newest tiles' loads).
+    const bool lagging = wave >= kQWaves / 2;
+    for (int t = 0; t < T::kAhead; ++t)
+        if (t < ntiles) issue(t, lds + T::k_stage(t));
+    if (ntiles >= T::kAhead)
+        wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
+    else
+        wait_vm_barrier<0>();
+    if (lagging) fence_barrier();
+
+    f32x16 s, dp;
+    bf16x8 dsf[2];
+    bf16x8 ring[kQAhead<D>];
+    auto body = [&](int t, auto full, auto stage) {
+        constexpr bool FULL = decltype(full)::value;
+        const bool more = t + T::kAhead < ntiles;
+        UL_LDS unsigned char *nx = lds + stage(t + T::kAhead);
+        if constexpr (FULL) {
+            dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, qf, dof, ring, stage(t - 1), stage(t), fo,
+                                                [&](int k) {
+                                                    if (more) issue_k(t + T::kAhead, k, nx);
+                                                });
+        } else {
+            if (more) issue(t + T::kAhead, nx);
+            auto none = [](int) {};
+            if (t >= 1 && visible(t - 1))
+                dq_gemm<D, true, false, 0>(dqacc, dsf, s, dp, qf, dof, ring, stage(t - 1), 0, fo, none);
+            if (t < ntiles && visible(t))
+                dq_gemm<D, false, true, 0>(dqacc, dsf, s, dp, qf, dof, ring, 0, stage(t), fo, none);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more)
+            wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
+        else
+            wait_vm_barrier<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        if (FULL || (t < ntiles && visible(t))) {
+            if constexpr (FULL)
+                dq_ds<false>(dsf, s, dp, lse2, Drow, kg, t * kDqKT, row, N, p.causal, c);
+            else
+                dq_ds<true>(dsf, s, dp, lse2, Drow, kg, t * kDqKT, row, N, p.causal, c);
+            dq_prefetch<D>(ring, stage(t), fo);
+        }
+        fence_barrier();
+    };
+    auto rt_stage = [](int x) { return (uint32_t)T::k_stage(x & (T::kStages - 1)); };
+    body(0, std::false_type{}, rt_stage);
+    int t0 = 1;
+    for (; t0 + T::kStages <= n_full; t0 += T::kStages) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            // x - t0 + 1 folds to a constant for every tile index body derives from t0 + J
+            (body(t0 + J, std::true_type{},
+                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+             ...);
+        }(std::make_integer_sequence<int, T::kStages>{});
     }
-    if (t < n_full) {
-        step(t, std::false_type{}, S0{});
-        ++t;
-        if (t < ntiles) step(t, std::true_type{}, S1{});
-        ++t;
-    }
-    for (; t + 1 < ntiles; t += 2) {
-        step(t, std::true_type{}, S0{});
-        step(t + 1, std::true_type{}, S1{});
-    }
-    if (t < ntiles) step(t, std::true_type{}, S0{});
+    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage);
+    if (!lagging) fence_barrier();
 
     // dQ = scale * (dQ^T)^T, rounded to bf16: lane column = query row, registers = head dim
     if (ok) {

@@ -115,6 +115,7 @@ __device__ __forceinline__ void fwd_gemm(FwdAcc<D> &acc, const bf16x8 (&pf)[4], 
                                          uint32_t kstage, const FragOffs<D> &o, Side &&side) {
     constexpr int EB = D / 32, KK = D / 16, HALF = 32 * D * 2;
     constexpr int NPV = PV ? 4 * EB : 0, NS = S ? 2 * KK : 0, NSTEP = NPV + NS;
+    static_assert(!PV || NPV >= kAhead, "the prefetched ring holds PV steps only");
     constexpr int EVERY = NSIDE > 0 ? NSTEP / NSIDE : 1;
     auto frag = [&](int st) -> bf16x8 {
         if (st < NPV) {
@@ -214,13 +215,6 @@ __device__ __forceinline__ void fwd_softmax(FwdAcc<D> &acc, f32x16 (&s)[2], bf16
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pf[i]));
     asm volatile("" : "+v"(acc.l));
-}
-
-// A workgroup barrier that the scheduler does not move work across.
-__device__ __forceinline__ void fence_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int D>

@@ -315,6 +315,13 @@ struct DmaTile {
     }
 };
 
+// A workgroup barrier that the scheduler does not move work across.
+__device__ __forceinline__ void fence_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and all of its LDS operations are done, then meet the other
 // waves (s_waitcnt encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 0).
