@@ -38,10 +38,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ============================================================================ pre kernel
 
+// Workspace layout: for each (b, h), N floats of lse2 (= lse log2 e) then N
+// floats of D, so both statistics of a query tile are one block apart.
 struct PreParams {
     const void *o, *dout;
     const float *lse;
-    float *lse2, *Dv;
+    float *stats;
     int64_t N;
     int32_t B, Hq, d;
     int32_t is_bf16;
@@ -73,9 +75,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
         const int64_t h = row % p.Hq;
         const int64_t bi = row / p.Hq;
         const int64_t i = bi % p.N, b = bi / p.N;
-        const int64_t o = (b * p.Hq + h) * p.N + i;
-        p.Dv[o] = acc;
-        p.lse2[o] = p.lse[o] * kLog2e;
+        const int64_t bh = b * p.Hq + h;
+        p.stats[(2 * bh) * p.N + i] = p.lse[bh * p.N + i] * kLog2e;
+        p.stats[(2 * bh + 1) * p.N + i] = acc;
     }
 }
 
@@ -106,7 +108,7 @@ constexpr int kQAhead = 2 * (D / 32) < 6 ? 2 * (D / 32) : 6;
 
 struct DqParams {
     const uint16_t *q, *k, *v, *dout;
-    const float *lse2, *Dv;
+    const float *stats;
     uint16_t *dq;
     int32_t N, B, Hq, Hkv;
     int32_t heads_per_wg, pos_blocks, head_groups, n_qblk;
@@ -263,9 +265,9 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
         dof[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + row * q_rs + kk * 16 + kg * 8)
                                : u32x4{0, 0, 0, 0});
     }
-    const int64_t so = ((int64_t)b * p.Hq + h) * N + (ok ? row : 0);
-    const float lse2 = ok ? p.lse2[so] : 0.f;
-    const float Drow = ok ? p.Dv[so] : 0.f;
+    const int64_t so = ((int64_t)b * p.Hq + h) * 2 * N + (ok ? row : 0);
+    const float lse2 = ok ? p.stats[so] : 0.f;
+    const float Drow = ok ? p.stats[so + N] : 0.f;
     // Retire these loads: inside the loop vmcnt counts only the tile loads.
     __builtin_amdgcn_s_waitcnt(0x70);
 
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     }
     auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
         const int j0 = t * kDqKT;
-        const uint32_t lim = (uint32_t)(N - 1 - j0) * row_bytes;
+        const uint32_t lim = (uint32_t)min(N - 1 - j0, kDqKT) * row_bytes;  // last key of the sequence
         dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
                  base + tile_lds + (u0 + k) * 1024);
     };
@@ -409,31 +411,39 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 
 // ============================================================================ bf16: dK/dV kernel
 //
-// 8 waves per workgroup, 128 keys of one KV head: waves 0-3 are producers and
-// waves 4-7 consumers; producer w and consumer w+4 share a SIMD and own the
-// same 32 keys.  The workgroup steps over 32-row query tiles of every query
-// head of the group, from the causal diagonal to N.
-//   producer, step s:  S = Q K^T, dP = dO V^T   (A = Q / dO rows from LDS,
-//                      B = K / V fragments held in registers), P = exp2(S c - lse2),
-//                      dS = P (dP - D); the bf16 P and dS fragments go to LDS
-//                      in the lane order of the consumer's B operand.
-//   consumer, step s-1: dV^T += dO^T P, dK^T += Q^T dS  (A = dO^T / Q^T by
-//                      transposed LDS reads), summed over the group's heads.
-// The producer's softmax VALU work overlaps the consumer's MFMAs on the same
-// SIMD, and each role stays inside a 256-register budget (2 waves per SIMD).
-// Q/dO tiles rotate through 3 LDS stages (being filled / produced / consumed);
-// P/dS through 2.
+// 8 waves per workgroup, 128 keys of one KV head: waves 0-3 are producers,
+// waves 4-7 consumers, and producer w shares a SIMD with consumer w+4.  The
+// workgroup steps over 32-row query tiles of every query head of the group,
+// from the end of the sequence down to the causal diagonal.
+//   producer w, step i:  for its 32 keys, S = Q K^T and dP = dO V^T  (A = Q /
+//                        dO rows from LDS, B = K / V fragments held in
+//                        registers), P = exp2(S c - lse2), dS = P (dP - D);
+//                        the bf16 P and dS fragments go to LDS in the lane
+//                        order of a B operand.
+//   consumer c, step i-1: for keys 64 (c/2) .. +64 and head dims 64 (c%2) ..
+//                        +64, dV^T += dO^T P and dK^T += Q^T dS  (A = dO^T / Q^T
+//                        by transposed LDS reads, B = the producers' P / dS),
+//                        summed over the group's heads.  Each A fragment feeds
+//                        the MFMAs of two 32-key blocks, which halves the
+//                        consumers' LDS reads against one 32-key block each.
+// Each step has two halves split by a barrier: in the first the producers
+// issue their 16 MFMAs while the consumers read their operands; in the second
+// the consumers issue their 16 MFMAs (with the tile loads between them) while
+// the producers do the softmax VALU work, store P / dS and read the next
+// step's operands.  Each role fits in 256 registers (2 waves per SIMD).  Q/dO
+// tiles rotate through 6 LDS stages (steps i-1 .. i+4), P/dS through 2.
 
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kKvPairs = 4;                          // producer/consumer pairs
-constexpr int kKeysPerWave = 32;
+constexpr int kKvPairs = 4;                          // producers (and consumers)
+constexpr int kKeysPerWave = 32;                     // keys of one producer
 constexpr int kKeysPerWg = kKvPairs * kKeysPerWave;  // 128
 constexpr int kQT = 32;                              // query rows per step
+constexpr int kKvAhead = 6;                          // A fragments read ahead of their MFMA
 
 struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
-    const float *lse2, *Dv;
+    const float *stats;
     uint16_t *dk, *dv;
     int32_t N, B, Hq, Hkv;
     int32_t n_kblk;
@@ -441,130 +451,156 @@ struct DkvParams {
     int32_t causal;
 };
 
+// LDS: the Q tiles of every stage, then the dO tiles, the statistics rows and
+// the two P/dS buffers.  Each region is addressed from a per-lane base
+// register and every stage / step offset inside it stays below 64 KB.
 template <int D>
 struct DkvTile {
-    static constexpr int kBytes = kQT * D * 2;          // one Q or dO tile
-    static constexpr int kStats = 2 * kQT * 4;          // lse2 then D, fp32
-    static constexpr int kStage = 2 * kBytes + kStats;  // Q, dO, stats
-    static constexpr int kPds = kKvPairs * 4 * 64 * 16; // P[2], dS[2] fragments per pair, per lane
-    static constexpr int kAhead = 4;                    // steps of loads in flight
-    static constexpr int kStages = kAhead + 2;          // + produced + consumed
-    static constexpr int kPdsStages = 2;
-    static constexpr int kPds0 = kStages * kStage;
-    static constexpr int kLds = kPds0 + kPdsStages * kPds;
-    __device__ static constexpr int stage(int st) { return st * kStage; }
-    __device__ static constexpr int pds(int st) { return kPds0 + st * kPds; }
+    static constexpr int kBytes = kQT * D * 2;                  // one Q or dO tile
+    static constexpr int kAhead = 5;                            // steps from a load to its use
+    static constexpr int kStages = kAhead + 1;                  // steps i-1 .. i+kAhead-1
+    static_assert(kStages % 2 == 0, "P/dS buffer parity follows the stage index");
+    static constexpr int kDoBase = kStages * kBytes;
+    static constexpr int kStatBytes = 2 * kQT * 4;              // lse2 then D, fp32
+    static constexpr int kStatBase = 2 * kStages * kBytes;
+    static constexpr int kPdsPair = 4 * 64 * 16;                // P[2], dS[2] fragments of one producer
+    static constexpr int kPds = kKvPairs * kPdsPair;            // one buffer
+    static constexpr int kPdsBase = kStatBase + kStages * kStatBytes;
+    static constexpr int kLds = kPdsBase + 2 * kPds;
+    static_assert(kDoBase <= 65536 && 2 * kPds <= 65536, "offsets must fit an LDS immediate");
+    __device__ static constexpr int q_stage(int st) { return st * kBytes; }
+    __device__ static constexpr int stat_stage(int st) { return st * kStatBytes; }
 };
 
-// Per-lane LDS offsets used inside the step loop (see precomputed lane offsets).
-template <int D>
-struct DkvOffs {
-    static constexpr int KK = D / 16, EB = D / 32;
-    uint32_t rm[KK];      // producer: Q / dO row fragment of k-step kk (row kperm(m))
-    uint32_t stat;        // producer: first of the 8 statistics rows of this lane group
-    uint32_t pds;         // both: this lane's P/dS fragment slot in its pair's block
-    uint32_t tr[EB][2];   // consumer: transposed Q / dO fragment halves, rows 0..15
-    __device__ __forceinline__ DkvOffs(int lane, int pair) {
-        const int m = lane & 31, kg = lane >> 5;
-        const int qrow = kperm(m);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) rm[kk] = rm_off<D>(qrow, kk * 2 + kg);
-        stat = 2 * DkvTile<D>::kBytes + kg * 8 * 4;
-        pds = (uint32_t)(pair * 4 * 64 + lane) * 16;
-        const TrAddr<D> ta(lane);
-#pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
-            tr[eb][0] = tr_off<D>(ta, eb * 32, 0);
-            tr[eb][1] = tr_off<D>(ta, eb * 32, 1);
-        }
-    }
-};
+// ---- producer
 
-// Producer step on the Q/dO tile at `tile` (stage base): S, dP -> P, dS
-// fragments -> the P/dS block at `pdsb`.  `masked` applies the causal diagonal
-// and the ragged ends (only the softmax block is duplicated for it).
+// S and dP of one step as a stream of 2 KK MFMAs, per k-step S then dP (A = Q
+// / dO row fragments of the tile at stage offset `qst`); the first kKvAhead
+// fragments are already in `ring` (read at the end of the previous step).
 template <int D>
-__device__ __forceinline__ void dkdv_produce(const bf16x8 *kf, const bf16x8 *vf,
-                                             const UL_LDS unsigned char *tile, UL_LDS unsigned char *pdsb,
-                                             const DkvOffs<D> &o, int kg, bool masked, int r0, int key,
-                                             int N, int causal, float c) {
-    using T = DkvTile<D>;
-    constexpr int KK = D / 16;
-    f32x16 s = zero16(), dp = zero16();
-    bf16x8 aq = lds_frag(tile, o.rm[0]), ad = lds_frag(tile + T::kBytes, o.rm[0]);
+__device__ __forceinline__ bf16x8 dkdv_sdp_frag(int st, uint32_t qst, const uint32_t *oq, const uint32_t *od) {
+    return lds_frag_at((st % 2 == 0 ? oq[st / 2] : od[st / 2]) + qst);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_sdp_prefetch(bf16x8 (&ring)[kKvAhead], uint32_t qst, const uint32_t *oq,
+                                                  const uint32_t *od) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        bf16x8 nq = aq, nd = ad;
-        if (kk + 1 < KK) {
-            nq = lds_frag(tile, o.rm[kk + 1]);
-            nd = lds_frag(tile + T::kBytes, o.rm[kk + 1]);
-        }
-        s = mfma32x32x16(aq, kf[kk], s);
-        dp = mfma32x32x16(ad, vf[kk], dp);
-        aq = nq;
-        ad = nd;
+    for (int st = 0; st < kKvAhead; ++st) ring[st] = dkdv_sdp_frag<D>(st, qst, oq, od);
+}
+
+// `side(k)`, k < NSIDE, runs between MFMAs spread over the stream (the tile
+// loads).
+template <int D, int NSIDE, typename Side>
+__device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const bf16x8 *kf, const bf16x8 *vf,
+                                         bf16x8 (&ring)[kKvAhead], uint32_t qst, const uint32_t *oq,
+                                         const uint32_t *od, Side &&side) {
+    constexpr int NSTEP = 2 * (D / 16), EVERY = NSTEP / NSIDE;
+    s = zero16();
+    dp = zero16();
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+        const bf16x8 a = ring[st % kKvAhead];
+        if (st + kKvAhead < NSTEP) ring[st % kKvAhead] = dkdv_sdp_frag<D>(st + kKvAhead, qst, oq, od);
+        if (st % 2 == 0)
+            s = mfma32x32x16(a, kf[st / 2], s);
+        else
+            dp = mfma32x32x16(a, vf[st / 2], dp);
+        if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // C register r of lane group kg holds query row ckey(r, kg): two runs of 8
-    // consecutive rows (16*hh + 8*kg ..), so the row statistics load as float4s.
-    float pv[16], dsv[16];
+}
+
+// The statistics of this lane group's 16 rows (lse2 and D for the 8-row runs
+// hh, rows 0-3 then 4-7 of each), read from a stage's block at `stat`.
+struct DkvStats {
+    f32x4 l[2][2], d[2][2];
+};
+
+__device__ __forceinline__ void dkdv_stats(DkvStats &t, uint32_t stat) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            t.l[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + hh * 64 + x * 16));
+            t.d[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + kQT * 4 + hh * 64 + x * 16));
+        }
+}
+
+// P = exp2(S c - lse2) (zero where MASK finds a key past the row or past N)
+// and dS = P (dP - D) as bf16 B fragments at this lane's slot `pds`.  C
+// register r of lane group kg holds query row ckey(r, kg): two runs of 8
+// consecutive rows (16*hh + 8*kg ..), whose statistics are in `t`.
+template <bool MASK>
+__device__ __forceinline__ void dkdv_softmax(const f32x16 &s, const f32x16 &dp, const DkvStats &t, uint32_t pds,
+                                             int kg, int r0, int key, int N, int causal, float c) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        const UL_LDS unsigned char *st = tile + o.stat + hh * 16 * 4;
-        const f32x4 l0 = *reinterpret_cast<const UL_LDS f32x4 *>(st);
-        const f32x4 l1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + 16);
-        const f32x4 d0 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4);
-        const f32x4 d1 = *reinterpret_cast<const UL_LDS f32x4 *>(st + kQT * 4 + 16);
+        const f32x4 l0 = t.l[hh][0], l1 = t.l[hh][1], d0 = t.d[hh][0], d1 = t.d[hh][1];
+        float pv[8], ds[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = hh * 8 + q;
-            const float lz = q < 4 ? l0[q] : l1[q - 4];
-            const float dz = q < 4 ? d0[q] : d1[q - 4];
-            pv[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lz));
-            dsv[r] = dp[r] - dz;
+            pv[q] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -(q < 4 ? l0[q] : l1[q - 4])));
+            if constexpr (MASK) {
+                const int i = r0 + ckey(r, kg);
+                pv[q] = (i >= N || key >= N || (causal && key > i)) ? 0.f : pv[q];
+            }
+            ds[q] = pv[q] * (dp[r] - (q < 4 ? d0[q] : d1[q - 4]));
         }
-    }
-    if (masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = r0 + ckey(r, kg);
-            if (i >= N || key >= N || (causal && key > i)) pv[r] = 0.f;
-        }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        float ds8[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) ds8[q] = pv[hh * 8 + q] * dsv[hh * 8 + q];
-        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + hh * 64 * 16) = __builtin_bit_cast(u32x4, pack8(pv + hh * 8));
-        *reinterpret_cast<UL_LDS u32x4 *>(pdsb + o.pds + (2 + hh) * 64 * 16) = __builtin_bit_cast(u32x4, pack8(ds8));
+        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + hh * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(pv));
+        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + (2 + hh) * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(ds));
     }
 }
 
-// Consumer step: dV^T += dO^T P ; dK^T += Q^T dS  (k = query rows, 2 steps of 16)
+// ---- consumer
+
+// The consumer's MFMAs of a step: for k-step ks (16 rows), head-dim block e2
+// of its half (EBC = D/64 blocks of 32) and dV / dK, one transposed A
+// fragment (dO^T / Q^T of the tile at `qst`) times the P / dS fragments of
+// its two 32-key blocks.
 template <int D>
-__device__ __forceinline__ void dkdv_consume(f32x16 *dkacc, f32x16 *dvacc, const UL_LDS unsigned char *tile,
-                                             const UL_LDS unsigned char *pdsb, const DkvOffs<D> &o) {
-    using T = DkvTile<D>;
-    constexpr int EB = D / 32;
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        pf[hh] = lds_frag(pdsb, o.pds + hh * 64 * 16);
-        dsf[hh] = lds_frag(pdsb, o.pds + (2 + hh) * 64 * 16);
+struct DkdvCons {
+    static constexpr int EBC = D / 64;                 // head-dim blocks per half
+    static constexpr int NA = 2 * EBC * 2;             // A fragments per step: ks x e2 x {dO^T, Q^T}
+    static constexpr int AH = NA < kKvAhead ? NA : kKvAhead;
+    uint32_t tq[EBC][2], td[EBC][2];                   // transposed Q / dO halves of the half's blocks
+    __device__ __forceinline__ bf16x8 frag(int st, uint32_t qst) const {
+        const int ks = st / (2 * EBC), e2 = (st / 2) % EBC;
+        const uint32_t at = qst + ks * 16 * D * 2;
+        const uint32_t *t = st % 2 == 0 ? td[e2] : tq[e2];
+        return lds_tr_frag_at(t[0] + at, t[1] + at);
     }
+    __device__ __forceinline__ void prefetch(bf16x8 (&ring)[AH], uint32_t qst) const {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+        for (int st = 0; st < AH; ++st) ring[st] = frag(st, qst);
+    }
+    // pb / db[kb2][ks]: P / dS B fragments of key block kb2, k-step ks;
+    // `side(k)`, k < NSIDE, runs between MFMAs spread over the stream
+    template <int NSIDE, typename Side>
+    __device__ __forceinline__ void run(f32x16 (&dvacc)[EBC][2], f32x16 (&dkacc)[EBC][2],
+                                        const bf16x8 (&pb)[2][2], const bf16x8 (&db)[2][2],
+                                        bf16x8 (&ring)[AH], uint32_t qst, Side &&side) const {
+        static_assert(NSIDE <= NA, "at most one load per MFMA step");
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb) {
-            const int rofs = ks * 16 * D * 2;
-            const bf16x8 ado = lds_tr_frag(tile + T::kBytes + rofs, o.tr[eb][0], o.tr[eb][1]);
-            const bf16x8 aq = lds_tr_frag(tile + rofs, o.tr[eb][0], o.tr[eb][1]);
-            dvacc[eb] = mfma32x32x16(ado, pf[ks], dvacc[eb]);
-            dkacc[eb] = mfma32x32x16(aq, dsf[ks], dkacc[eb]);
+        for (int st = 0; st < NA; ++st) {
+            const bf16x8 a = ring[st % AH];
+            if (st + AH < NA) ring[st % AH] = frag(st + AH, qst);
+            const int ks = st / (2 * EBC), e2 = (st / 2) % EBC;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                if (st % 2 == 0)
+                    dvacc[e2][kb2] = mfma32x32x16(a, pb[kb2][ks], dvacc[e2][kb2]);
+                else
+                    dkacc[e2][kb2] = mfma32x32x16(a, db[kb2][ks], dkacc[e2][kb2]);
+            }
+#pragma unroll
+            for (int k = 0; k < NSIDE; ++k)
+                if (k * NA / NSIDE == st) side(k);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-}
+};
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParams p) {
@@ -572,6 +608,8 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     UL_LDS unsigned char *lds = (UL_LDS unsigned char *)smem_raw;
     using T = DkvTile<D>;
     using Tile = DmaTile<D, kQT>;
+    constexpr int KK = D / 16;
+    static_assert(D == 128 || D == 64, "head_dim");
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kg = lane >> 5;
@@ -587,8 +625,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     const int N = p.N;
     const int64_t q_rs = (int64_t)p.Hq * D;
     const int kb0 = kblk * kKeysPerWg;
-    const int jw0 = kb0 + pair * kKeysPerWave;  // the pair's first key
-    const int key = jw0 + m;                    // this lane's key (C column)
+    const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
     // Steps: 32-row tiles from the end of the sequence down to the causal
     // diagonal, the group's query heads innermost.  Every workgroup walks the
@@ -612,77 +649,34 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         }
     };
     const Cur first{0, 0, (nqt - 1) * kQT};
-    const float c = p.scale_log2;
-    const DkvOffs<D> o(lane, pair);
 
-    // Direct loads of a step into its LDS stage: the Q and dO tiles are split
-    // evenly over the 8 waves (each wave's share lies in one of the two), and
-    // the last wave also fetches the 32 lse2 and D values, one dword per lane.
-    // Rows past N re-read row N-1 (masked by the producer).
-    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvWaves;  // per step; the last wave has one more
-    static_assert(2 * Tile::INSTR % kKvWaves == 0 && Tile::INSTR % kDmaPerWave == 0,
-                  "Q and dO tiles split evenly over the waves");
-    const bool loads_do = wave * kDmaPerWave >= Tile::INSTR;
-    const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
-    const uint16_t *tens = loads_do ? p.dout : p.q;
-    const int tile_lds = loads_do ? T::kBytes : 0;
-    const uint32_t row_bytes = (uint32_t)q_rs * 2;
-    int dma_row[kDmaPerWave];
-    uint32_t dma_gran[kDmaPerWave];
-#pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {
-        dma_row[k] = Tile::row(u0 + k, lane);
-        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
-    }
-    const int64_t dv_delta = (const char *)p.Dv - (const char *)p.lse2;
-    const bool stats_wave = wave == kKvWaves - 1;
-    auto issue = [&](const Cur &cu, UL_LDS unsigned char *base) {
-        const int lim = N - 1 - cu.r0;  // last valid row within the tile
-        const int h = g * grp + cu.hi;
-        const uint16_t *tb = tens + (((int64_t)b * N + cu.r0) * p.Hq + h) * D;
-#pragma unroll
-        for (int k = 0; k < kDmaPerWave; ++k)
-            dma_b128(tb, (uint32_t)min(dma_row[k], lim) * row_bytes + dma_gran[k],
-                     base + tile_lds + (u0 + k) * 1024);
-        if (stats_wave) {
-            const char *sb = (const char *)(p.lse2 + ((int64_t)b * p.Hq + h) * N + cu.r0);
-            const int r = min(lane & (kQT - 1), lim);
-            // lanes 0..31 read lse2, lanes 32..63 read D (a fixed distance away)
-            if (lane < kQT)
-                dma_b32(sb, (uint32_t)r * 4, base + 2 * T::kBytes);
-            else
-                dma_b32(sb + dv_delta, (uint32_t)r * 4, base + 2 * T::kBytes);
-        }
-    };
-    // the pair's keys see at least one row of a step starting at row r0
-    auto visible = [&](int r0) { return (!p.causal || jw0 <= r0 + kQT - 1) && jw0 < N; };
+    // Zero the LDS: the step before the first reads never-loaded stage and
+    // P/dS memory, which must hold zeros (P = dS = 0 contribute nothing).
+    for (int x = tid; x < T::kLds / 16; x += kKvThreads)
+        *reinterpret_cast<UL_LDS u32x4 *>(lds + x * 16) = u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    fence_barrier();
 
-    // Loads always run kAhead steps ahead (past the last step they re-read it
-    // into a free stage), so every wave has the same number in flight at each
-    // barrier: waiting for all but the newest (kAhead-1) steps' worth leaves
-    // the oldest one landed.
-    Cur iss = first;
-    [&]<int... J>(std::integer_sequence<int, J...>) {
-        ((issue(iss, lds + T::stage(J)), advance(iss)), ...);
-    }(std::make_integer_sequence<int, T::kAhead>{});
-    wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
-
-    // Iteration i (LDS stage i % 6, unrolled by 6 so stages are immediates):
-    // issue step i+4, producers handle step i, consumers step i-1; the
-    // barrier at the end waits for step i+1, the oldest load still in flight.
-    auto run = [&](auto body) {
+    // Step halves for i = 0 .. nsteps (unrolled by the stage count so stage
+    // offsets are constants): stage i % 6 holds step i's tiles, P/dS buffer
+    // i % 2 its fragments.  Every step runs in full: where a producer's keys
+    // see none of a step's rows the mask makes P and dS zero, and the
+    // iteration past the last step works on a re-read of the last step's
+    // tiles (finite, unused).
+    auto run = [&](auto half_a, auto half_b) {
         for (int i0 = 0; i0 <= nsteps; i0 += T::kStages) {
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                ((i0 + J <= nsteps ? body(i0 + J, std::integral_constant<int, J>{}) : void()), ...);
+                ((i0 + J <= nsteps ? (half_a(i0 + J, std::integral_constant<int, J>{}),
+                                      half_b(i0 + J, std::integral_constant<int, J>{}))
+                                   : void()),
+                 ...);
             }(std::make_integer_sequence<int, T::kStages>{});
         }
-        // no load may still be writing this workgroup's LDS when it exits
-        __builtin_amdgcn_s_waitcnt(0x70);
     };
 
     if (producer) {
-        // K and V rows of the pair's 32 keys as B fragments (column = key, k = head dim)
-        constexpr int KK = D / 16;
+        const int key = kb0 + pair * kKeysPerWave + m;  // this lane's key (C column)
+        // K and V rows of the producer's 32 keys as B fragments (column = key, k = head dim)
         bf16x8 kf[KK], vf[KK];
         {
             const bool ok = key < N;
@@ -694,66 +688,199 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
                 vf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(vr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
             }
         }
-        // Retire these loads here: inside the loop vmcnt must count only the
-        // stage loads, or a wait for a fragment would also wait for the
-        // newest stage.
         __builtin_amdgcn_s_waitcnt(0x70);
+        // absolute LDS addresses: Q / dO row fragments (stage 0), statistics
+        // of this lane group's rows (stage 0), this lane's P/dS slot (buffer 0)
+        uint32_t oq[KK], od[KK];
+        {
+            const int qrow = kperm(m);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                oq[kk] = lbase + rm_off<D>(qrow, kk * 2 + kg);
+                od[kk] = oq[kk] + T::kDoBase;
+                asm volatile("" : "+v"(oq[kk]));
+                asm volatile("" : "+v"(od[kk]));
+            }
+        }
+        uint32_t stat = lbase + T::kStatBase + kg * 8 * 4;
+        uint32_t pds = lbase + T::kPdsBase + pair * T::kPdsPair + lane * 16;
+        asm volatile("" : "+v"(stat));
+        asm volatile("" : "+v"(pds));
+        const float c = p.scale_log2;
+
+        fence_barrier();  // the consumers' first loads have landed
+        bf16x8 ring[kKvAhead];
+        f32x16 s, dp;
+        DkvStats stats;
         Cur cmp = first;
-        run([&](int i, auto stage) {
-            constexpr int ST = decltype(stage)::value, NN = (ST + T::kAhead) % T::kStages, PD = ST % 2;
-            issue(iss, lds + T::stage(NN));
-            advance(iss);
-            if (i < nsteps && visible(cmp.r0)) {
+        dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
+        dkdv_stats(stats, stat + T::stat_stage(0));
+        run(
+            [&](int, auto stage) {  // MFMA half: S and dP of step i
+                constexpr int ST = decltype(stage)::value;
+                dkdv_sdp<D, 1>(s, dp, kf, vf, ring, T::q_stage(ST), oq, od, [](int) {});
+                fence_barrier();
+            },
+            [&](int, auto stage) {  // P / dS of step i, then step i+1's operands
+                constexpr int ST = decltype(stage)::value, NX = (ST + 1) % T::kStages;
                 const int r0 = cmp.r0;
                 const bool masked = (p.causal && r0 < kb0 + kKeysPerWg) || r0 + kQT > N ||
                                     kb0 + kKeysPerWg > N;
-                dkdv_produce<D>(kf, vf, lds + T::stage(ST), lds + T::pds(PD), o, kg, masked, r0, key, N,
-                                p.causal, c);
-            }
-            advance(cmp);
-            wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
-        });
+                if (masked)
+                    dkdv_softmax<true>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
+                else
+                    dkdv_softmax<false>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
+                advance(cmp);
+                dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
+                dkdv_stats(stats, stat + T::stat_stage(NX));
+                // P / dS stored (and the operands read) before the barrier
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+                fence_barrier();
+            });
         return;
     }
 
-    constexpr int EB = D / 32;
-    f32x16 dkacc[EB], dvacc[EB];
+    // ---- consumers: for keys 64 kh .. +64 and head dims 64 eh .. +64
+    const int kh = pair >> 1, eh = pair & 1;
+    // Direct loads of a step into its LDS stage, issued between the
+    // consumers' MFMAs: the Q and dO tiles are split evenly over the 4
+    // consumers (each one's share inside one of the two); the last consumer
+    // also fetches the 32 lse2 and D values, one dword per lane.  Rows past N
+    // re-read row N-1 (masked by the producers).
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvPairs;
+    static_assert(2 * Tile::INSTR % kKvPairs == 0 && Tile::INSTR % kDmaPerWave == 0,
+                  "Q and dO tiles split evenly over the consumers");
+    const bool loads_do = pair * kDmaPerWave >= Tile::INSTR;
+    const int u0 = (pair * kDmaPerWave) % Tile::INSTR;
+    const uint16_t *tens = loads_do ? p.dout : p.q;
+    const int tile_lds = loads_do ? T::kDoBase : 0;
+    const uint32_t row_bytes = (uint32_t)q_rs * 2;
+    uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
 #pragma unroll
-    for (int eb = 0; eb < EB; ++eb) {
-        dkacc[eb] = zero16();
-        dvacc[eb] = zero16();
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
+        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
     }
-    Cur cmp = first;
-    run([&](int i, auto stage) {
-        constexpr int ST = decltype(stage)::value, NN = (ST + T::kAhead) % T::kStages;
-        constexpr int PV = (ST + T::kStages - 1) % T::kStages, PD = (ST + 1) % 2;
-        issue(iss, lds + T::stage(NN));
-        advance(iss);
-        if (i >= 1) {
-            if (visible(cmp.r0)) dkdv_consume<D>(dkacc, dvacc, lds + T::stage(PV), lds + T::pds(PD), o);
-            advance(cmp);
+    const bool stats_wave = pair == kKvPairs - 1;
+    // load k of this consumer's share of step `cu` into stage st (k =
+    // kDmaPerWave: the statistics, on the last consumer)
+    auto issue_k = [&](const Cur &cu, int st, int k) {
+        const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
+        const int h = g * grp + cu.hi;
+        if (k < kDmaPerWave) {
+            const uint16_t *tb = tens + (((int64_t)b * N + cu.r0) * p.Hq + h) * D;
+            dma_b128(tb, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
+                     lds + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
+        } else if (stats_wave) {
+            // lanes 0..31 read the lse2 rows, lanes 32..63 the D rows N floats
+            // later (each lane lands at its own dword of the stage's block)
+            const float *sl = p.stats + ((int64_t)b * p.Hq + h) * 2 * N + cu.r0;
+            const int r = min(lane & (kQT - 1), lim);
+            if (lane < kQT)
+                dma_b32(sl, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
+            else
+                dma_b32(sl + N, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
         }
-        wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
-    });
+    };
+    auto issue = [&](const Cur &cu, int st) {
+#pragma unroll
+        for (int k = 0; k <= kDmaPerWave; ++k) issue_k(cu, st, k);
+    };
+    // Loads run kAhead steps ahead (past the last step they re-read it into
+    // a free stage), so every consumer has the same number in flight at each
+    // wait.  The MFMA half of step i issues step i+kAhead-1; before the
+    // barrier ending the first half of step i (which follows the loads of
+    // step i+kAhead-2) step i+1 must have landed: all but the newest kAhead-3
+    // steps' worth.
+    auto wait_next = [&]() {
+        if (stats_wave)
+            wait_vm<(T::kAhead - 3) * (kDmaPerWave + 2)>();
+        else
+            wait_vm<(T::kAhead - 3) * kDmaPerWave>();
+    };
+    Cur iss = first;
+    [&]<int... J>(std::integer_sequence<int, J...>) {
+        ((issue(iss, J), advance(iss)), ...);
+    }(std::make_integer_sequence<int, T::kAhead - 1>{});
+    wait_vm<0>();  // the first steps have landed
+    fence_barrier();
 
-    // dK = scale * acc, dV = acc (bf16); lane column = key, registers = head dim
-    if (key < N) {
-        uint16_t *dkr = p.dk + (((int64_t)b * N + key) * p.Hkv + g) * D;
-        uint16_t *dvr = p.dv + (((int64_t)b * N + key) * p.Hkv + g) * D;
+    // absolute LDS addresses: transposed Q / dO halves of the head-dim
+    // blocks, and this lane's slot in the P/dS blocks of the key half
+    using Cons = DkdvCons<D>;
+    constexpr int EBC = Cons::EBC;
+    Cons cons;
+    {
+        const TrAddr<D> ta(lane);
 #pragma unroll
-        for (int eb = 0; eb < EB; ++eb)
+        for (int e2 = 0; e2 < EBC; ++e2)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 k4, v4;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    k4[q] = (__bf16)(dkacc[eb][r4 * 4 + q] * p.scale);
-                    v4[q] = (__bf16)(dvacc[eb][r4 * 4 + q]);
-                }
-                const int e = eb * 32 + r4 * 8 + kg * 4;
-                *reinterpret_cast<u32x2 *>(dkr + e) = __builtin_bit_cast(u32x2, k4);
-                *reinterpret_cast<u32x2 *>(dvr + e) = __builtin_bit_cast(u32x2, v4);
+            for (int x = 0; x < 2; ++x) {
+                cons.tq[e2][x] = lbase + tr_off<D>(ta, (eh * EBC + e2) * 32, x);
+                cons.td[e2][x] = cons.tq[e2][x] + T::kDoBase;
+                asm volatile("" : "+v"(cons.tq[e2][x]));
+                asm volatile("" : "+v"(cons.td[e2][x]));
             }
+    }
+    uint32_t pds = lbase + T::kPdsBase + 2 * kh * T::kPdsPair + lane * 16;
+    asm volatile("" : "+v"(pds));
+    f32x16 dvacc[EBC][2], dkacc[EBC][2];
+#pragma unroll
+    for (int e2 = 0; e2 < EBC; ++e2)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            dvacc[e2][k2] = zero16();
+            dkacc[e2][k2] = zero16();
+        }
+    bf16x8 ring[Cons::AH], pb[2][2], db[2][2];
+    run(
+        [&](int, auto stage) {  // operands of step i-1; step i+1 landed
+            constexpr int ST = decltype(stage)::value, PV = (ST + T::kStages - 1) % T::kStages;
+            const uint32_t buf = pds + (PV % 2) * T::kPds;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    pb[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + ks * 64 * 16);
+                    db[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + (2 + ks) * 64 * 16);
+                }
+            cons.prefetch(ring, T::q_stage(PV));
+            wait_next();
+            fence_barrier();
+        },
+        [&](int, auto stage) {  // MFMA half: dV and dK of step i-1, loads of step i+kAhead-1
+            constexpr int ST = decltype(stage)::value, PV = (ST + T::kStages - 1) % T::kStages;
+            constexpr int NN = (ST + T::kAhead - 1) % T::kStages;
+            cons.template run<kDmaPerWave + 1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV),
+                                               [&](int k) { issue_k(iss, NN, k); });
+            advance(iss);
+            fence_barrier();
+        });
+    // no load may still be writing this workgroup's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(0x70);
+
+    // dK = scale * acc, dV = acc (bf16): lane column = key, registers = head dim
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const int key = kb0 + (2 * kh + k2) * kKeysPerWave + m;
+        if (key < N) {
+            uint16_t *dkr = p.dk + (((int64_t)b * N + key) * p.Hkv + g) * D;
+            uint16_t *dvr = p.dv + (((int64_t)b * N + key) * p.Hkv + g) * D;
+#pragma unroll
+            for (int e2 = 0; e2 < EBC; ++e2)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    bf16x4 k4, v4;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        k4[q] = (__bf16)(dkacc[e2][k2][r4 * 4 + q] * p.scale);
+                        v4[q] = (__bf16)(dvacc[e2][k2][r4 * 4 + q]);
+                    }
+                    const int e = (eh * EBC + e2) * 32 + r4 * 8 + kg * 4;
+                    *reinterpret_cast<u32x2 *>(dkr + e) = __builtin_bit_cast(u32x2, k4);
+                    *reinterpret_cast<u32x2 *>(dvr + e) = __builtin_bit_cast(u32x2, v4);
+                }
+        }
     }
 }
 
@@ -764,7 +891,8 @@ constexpr int kF32Keys = 32;
 
 struct BwdF32Params {
     const float *q, *k, *v, *dout;
-    const float *lse, *Dv;  // lse in natural-log units
+    const float *lse;    // natural-log units
+    const float *stats;  // the workspace statistics (D is read from it)
     float *dq, *dk, *dv;
     int64_t N;
     int32_t B, Hq, Hkv;
@@ -799,7 +927,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
     }
     const int64_t so = ((int64_t)b * p.Hq + h) * N + ri;
     const float lse = valid ? p.lse[so] : 0.f;
-    const float Di = valid ? p.Dv[so] : 0.f;
+    const float Di = valid ? p.stats[so + ((int64_t)b * p.Hq + h + 1) * N] : 0.f;
     const int64_t blk_last = (int64_t)rblk * kF32Rows + kF32Rows - 1;
     const int64_t kend = p.causal ? (blk_last + 1 < N ? blk_last + 1 : N) : N;
     for (int64_t j0 = 0; j0 < kend; j0 += kF32Keys) {
@@ -878,7 +1006,7 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
                 const int64_t i = i0 + tid;
                 const int64_t so = ((int64_t)b * p.Hq + h) * N + i;
                 ls[tid] = i < N ? p.lse[so] : 0.f;
-                Ds[tid] = i < N ? p.Dv[so] : 0.f;
+                Ds[tid] = i < N ? p.stats[so + ((int64_t)b * p.Hq + h + 1) * N] : 0.f;
             }
             __syncthreads();
             for (int ii = 0; ii < kF32KvRows; ++ii) {
@@ -916,12 +1044,12 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t /*dtype*/) {
     const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
-    return 2 * round256(rows * sizeof(float));
+    return round256(2 * rows * sizeof(float));
 }
 
-static hipError_t launch_pre(const void *o, const void *dout, const float *lse, float *lse2,
-                             float *Dv, const AttnShape &s, bool bf16, hipStream_t stream) {
-    PreParams pp{o, dout, lse, lse2, Dv, s.N, (int32_t)s.B, s.Hq, s.d, bf16 ? 1 : 0};
+static hipError_t launch_pre(const void *o, const void *dout, const float *lse, float *stats,
+                             const AttnShape &s, bool bf16, hipStream_t stream) {
+    PreParams pp{o, dout, lse, stats, s.N, (int32_t)s.B, s.Hq, s.d, bf16 ? 1 : 0};
     const int64_t rows = s.B * s.N * s.Hq;
     const int64_t blocks = (rows + 15) / 16;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -932,12 +1060,10 @@ static hipError_t launch_pre(const void *o, const void *dout, const float *lse, 
 hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, const void *o,
                                 const void *dout, const float *lse, void *dq, void *dk, void *dv,
                                 void *ws, const AttnShape &s, int stages, hipStream_t stream) {
-    const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
-    float *lse2 = static_cast<float *>(ws);
-    float *Dv = reinterpret_cast<float *>(static_cast<char *>(ws) + round256(rows * sizeof(float)));
+    float *stats = static_cast<float *>(ws);
     hipError_t err = hipSuccess;
     if (stages & UL_BWD_PREP) {
-        err = launch_pre(o, dout, lse, lse2, Dv, s, true, stream);
+        err = launch_pre(o, dout, lse, stats, s, true, stream);
         if (err != hipSuccess) return err;
     }
 
@@ -946,8 +1072,7 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     dp.k = static_cast<const uint16_t *>(k);
     dp.v = static_cast<const uint16_t *>(v);
     dp.dout = static_cast<const uint16_t *>(dout);
-    dp.lse2 = lse2;
-    dp.Dv = Dv;
+    dp.stats = stats;
     dp.dq = static_cast<uint16_t *>(dq);
     dp.N = (int32_t)s.N;
     dp.B = (int32_t)s.B;
@@ -970,8 +1095,7 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     kp.k = dp.k;
     kp.v = dp.v;
     kp.dout = dp.dout;
-    kp.lse2 = lse2;
-    kp.Dv = Dv;
+    kp.stats = stats;
     kp.dk = static_cast<uint16_t *>(dk);
     kp.dv = static_cast<uint16_t *>(dv);
     kp.N = (int32_t)s.N;
@@ -1016,15 +1140,13 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
 hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
                                const float *dout, const float *lse, float *dq, float *dk,
                                float *dv, void *ws, const AttnShape &s, int stages, hipStream_t stream) {
-    const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
-    float *lse2 = static_cast<float *>(ws);
-    float *Dv = reinterpret_cast<float *>(static_cast<char *>(ws) + round256(rows * sizeof(float)));
+    float *stats = static_cast<float *>(ws);
     hipError_t err = hipSuccess;
     if (stages & UL_BWD_PREP) {
-        err = launch_pre(o, dout, lse, lse2, Dv, s, false, stream);
+        err = launch_pre(o, dout, lse, stats, s, false, stream);
         if (err != hipSuccess) return err;
     }
-    BwdF32Params p{q, k, v, dout, lse, Dv, dq, dk, dv, s.N, (int32_t)s.B, s.Hq, s.Hkv,
+    BwdF32Params p{q, k, v, dout, lse, stats, dq, dk, dv, s.N, (int32_t)s.B, s.Hq, s.Hkv,
                    s.scale, s.causal, 0};
     p.n_blk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
     const int64_t dq_items = (int64_t)p.n_blk * p.B * p.Hq;

@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // load k of this wave's share of tile t into the stage at `base`
     auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
         const int j0 = t * kKT;
-        const uint32_t lim = (uint32_t)(N - 1 - j0) * row_bytes;  // last key of the sequence
+        const uint32_t lim = (uint32_t)min(N - 1 - j0, kKT) * row_bytes;  // last key of the sequence
         dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
                  base + tile_lds + (u0 + k) * 1024);
     };

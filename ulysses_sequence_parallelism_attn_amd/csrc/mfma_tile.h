@@ -324,11 +324,17 @@ __device__ __forceinline__ void fence_barrier() {
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and all of its LDS operations are done, then meet the other
-// waves (s_waitcnt encoding: vmcnt[3:0], expcnt[6:4] = 7, lgkmcnt[11:8] = 0).
+// waves (s_waitcnt encoding: vmcnt = {simm[15:14], simm[3:0]}, expcnt[6:4] = 7,
+// lgkmcnt[11:8] = 0).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-    static_assert(N >= 0 && N < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x70 | N);
+    wait_vm<N>();
     asm volatile("s_barrier" ::: "memory");
 }
 
