@@ -10,6 +10,10 @@ One step is one pass of the whole path over one batch of synthetic input:
   3. ul_attn_bwd: its dQ, dK, dV;
   4. ul_relayout_h2s of the [3, 4, 65536, 8, 128] head-sharded stack (the reverse exchange).
 
+A second measurement, `fused_relayout`, times the same rank's forward and backward through
+the token-strided entry points on sequence-sharded world tensors, i.e. the step with both
+relayouts fused into the attention's own loads and stores.
+
 The backward runs as its three C-ABI stages (D/lse preparation, the dQ pass, the dK/dV
 pass) with events between them, so each kernel's duration is measured on the stream it
 runs on; the `roofline` object reports the longest one against its peak.
@@ -139,6 +143,51 @@ def cpu_baseline(st: dict, wl, n_prefix: int) -> dict:
     }
 
 
+def fused_step(B, torch, q, k, v, do, wl, P, args, ms_relayout_path) -> dict:
+    """The same rank's forward and backward with the relayouts fused away: the token-strided
+    calls read the rank's head slice (rank P-1, the largest offsets) straight out of
+    sequence-sharded world tensors [B, N, P*H, d] and write O, dQ, dK, dV into world-layout
+    buffers.  Timed like the main step (warmup, then `steps` back-to-back passes)."""
+    dev = q.device
+    r = P - 1
+    qs, ks = slice(r * wl.Hq, (r + 1) * wl.Hq), slice(r * wl.Hkv, (r + 1) * wl.Hkv)
+    shape_q, shape_kv = (wl.B, wl.N, P * wl.Hq, wl.d), (wl.B, wl.N, P * wl.Hkv, wl.d)
+    Qw, Ow, dOw, dQw = (torch.empty(shape_q, dtype=q.dtype, device=dev) for _ in range(4))
+    Kw, Vw, dKw, dVw = (torch.empty(shape_kv, dtype=q.dtype, device=dev) for _ in range(4))
+    Qw[:, :, qs].copy_(q)
+    dOw[:, :, qs].copy_(do)
+    Kw[:, :, ks].copy_(k)
+    Vw[:, :, ks].copy_(v)
+    views = dict(q=Qw[:, :, qs], k=Kw[:, :, ks], v=Vw[:, :, ks], o=Ow[:, :, qs], do=dOw[:, :, qs],
+                 dq=dQw[:, :, qs], dk=dKw[:, :, ks], dv=dVw[:, :, ks])
+    lse = torch.empty((wl.B, wl.Hq, wl.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.workspace_bytes(wl.B, wl.N, wl.Hq, wl.Hkv, wl.d, B.UL_BF16),
+                     dtype=torch.uint8, device=dev)
+    vw = views  # short name for the step body
+
+    def step():
+        B.attn_fwd(vw["q"], vw["k"], vw["v"], wl.scale, True, out=vw["o"], lse=lse)
+        B.attn_bwd(vw["q"], vw["k"], vw["v"], vw["o"], vw["do"], lse, wl.scale, True, workspace=ws,
+                   dq=vw["dq"], dk=vw["dk"], dv=vw["dv"])
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    return {"ms_per_step": ms,
+            "tflops": (wl.flops_fwd() + wl.flops_bwd()) / (ms * 1e-3) / 1e12,
+            "tokens_per_s": wl.B * wl.N / (ms * 1e-3),
+            "speedup_vs_relayout_path": ms_relayout_path / ms,
+            "rank": r, "q_tok_stride": views["q"].stride(1), "kv_tok_stride": views["k"].stride(1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +195,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="attention workload id (default 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the strided (relayout-free) variant of the step")
     ap.add_argument("--cpu-prefix", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
@@ -313,6 +364,8 @@ def main() -> int:
         "roofline_all": roof,
         "kernel_hash": kernel_hash(),
     }
+    if not args.no_fused:
+        out["fused_relayout"] = fused_step(B, torch, q, k, v, do, wl, P, args, ms_per_step)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, wl, min(args.cpu_prefix, wl.N))
     print(json.dumps(out), flush=True)

@@ -15,7 +15,10 @@
  *   ul_attn_fwd       causal (or full) softmax attention over the full N for a
  *                     slice of query heads with grouped KV heads, also
  *                     returning the per-row logsumexp;
- *   ul_attn_bwd       its gradient (dQ, dK, dV).
+ *   ul_attn_bwd       its gradient (dQ, dK, dV);
+ *   ul_attn_*_strided the same on token-strided views, so that a rank's head
+ *                     slice is read from and written to sequence-sharded
+ *                     buffers in place (no relayout pass around attention).
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  No call
@@ -24,7 +27,8 @@
  *    kernels on `stream` (a hipStream_t passed as void*, NULL = the null
  *    stream) and returns.  Results are ready when the stream reaches that
  *    point.  Calls are thread-safe.
- *  - All tensors are dense row-major (C order).
+ *  - All tensors are row-major (C order) and dense, except the token-strided
+ *    views that the *_strided calls take.
  *  - Outputs are fully overwritten, never accumulated into.
  *  - Errors are reported only through the returned status.  Validation runs
  *    before any HIP call, so an invalid call enqueues nothing.
@@ -88,6 +92,37 @@ ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, floa
                       float softmax_scale, int32_t causal, int32_t dtype, void *stream);
 
 /*
+ * ul_attn_fwd on token-strided tensors: the head slice of one rank read from,
+ * and written to, token-major buffers that hold more heads than the rank's,
+ * so that no separate relayout pass runs on either side of the attention.
+ * (The first all-to-all of "How Does Ulysses Sequence Parallelism Actually
+ * Work?" hands each GPU all positions of a slice of heads, and the second
+ * reverses it; in the world view of one memory that slice is a strided view.)
+ *
+ * Element (b, t, h, e) of q and o is at
+ *     q[(b*N + t) * q_tok_stride + h*head_dim + e]    (o likewise with o_tok_stride)
+ * and element (b, t, g, e) of k and v at
+ *     k[(b*N + t) * k_tok_stride + g*head_dim + e]    (v likewise with v_tok_stride).
+ * The pointers are the addresses of element (0, 0, 0, 0), i.e. already offset
+ * to the first head of the slice.  Example: rank r of P reading its Hq query
+ * heads out of a sequence-sharded world tensor x[N][P*Hq][head_dim] passes
+ * q = x + r*Hq*head_dim and q_tok_stride = P*Hq*head_dim.
+ *
+ * Strides are in elements, at least (heads of that tensor) * head_dim, a
+ * multiple of 16 bytes, and at most 16 MiB; otherwise SHAPE (too small or too
+ * large) or ALIGNMENT (not a 16-byte multiple).  lse stays dense [B][Hq][N].
+ * OVERLAP: an output shares a byte with an input or another output (tensors
+ * with equal strides are compared row by row, so disjoint head slices of one
+ * buffer are accepted).  Everything else is as ul_attn_fwd, which is this
+ * call with q/o strides Hq*head_dim and k/v strides Hkv*head_dim.
+ */
+ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                              int64_t o_tok_stride, float softmax_scale, int32_t causal,
+                              int32_t dtype, void *stream);
+
+/*
  * Device workspace bytes that ul_attn_bwd needs for these sizes (a multiple
  * of 256).  Returns 0 for invalid sizes.
  */
@@ -144,6 +179,24 @@ ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const
                              void *dv, void *workspace, size_t workspace_bytes, int64_t B,
                              int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
                              float softmax_scale, int32_t causal, int32_t dtype, void *stream);
+
+/*
+ * ul_attn_bwd (all three stages) on token-strided tensors, with the layout
+ * rules of ul_attn_fwd_strided: q, o, dout and dq hold Hq heads per token,
+ * k, v, dk and dv Hkv heads, each tensor with its own token stride in
+ * elements.  dq, dk and dv may be disjoint head slices of one buffer (for
+ * example a packed [N][Hq + 2*Hkv][head_dim] gradient of a fused QKV
+ * projection).  lse and the workspace stay dense.  Errors as ul_attn_bwd plus
+ * the stride errors of ul_attn_fwd_strided.
+ */
+ul_status ul_attn_bwd_strided(const void *q, const void *k, const void *v, const void *o,
+                              const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                              void *workspace, size_t workspace_bytes, int64_t B, int64_t N,
+                              int32_t Hq, int32_t Hkv, int32_t head_dim, int64_t q_tok_stride,
+                              int64_t k_tok_stride, int64_t v_tok_stride, int64_t o_tok_stride,
+                              int64_t dout_tok_stride, int64_t dq_tok_stride,
+                              int64_t dk_tok_stride, int64_t dv_tok_stride, float softmax_scale,
+                              int32_t causal, int32_t dtype, void *stream);
 
 /*
  * Sequence-sharded -> head-sharded relayout (the first all-to-all of the

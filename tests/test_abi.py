@@ -30,7 +30,8 @@ def addr(i):
 
 def test_exports_every_declared_symbol(L):
     names = B.declared_functions()
-    assert set(names) == {"ul_attn_fwd", "ul_attn_bwd", "ul_attn_bwd_stages",
+    assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_bwd",
+                          "ul_attn_bwd_stages", "ul_attn_bwd_strided",
                           "ul_attn_bwd_workspace_bytes", "ul_relayout_s2h", "ul_relayout_h2s",
                           "ul_status_str"}
     for n in names:
@@ -111,6 +112,74 @@ def test_bwd_validation(L, kw, code):
 @pytest.mark.parametrize("stages", [0, 8, 9, -1])
 def test_bwd_stage_mask_validation(L, stages):
     assert bwd(L, stages=stages) == 4
+
+
+# ---- token-strided calls: a rank's head slice of world-layout buffers
+
+W = 32 * 128  # token stride (elements) of a [N][32][128] world tensor
+
+
+def fwd_s(L, q=None, k=None, v=None, o=None, lse=None, qs=W, ks=W, vs=W, os_=W, N=128, Hq=8,
+          Hkv=2, d=128, dtype=B.UL_BF16):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    o = addr(3) if o is None else o
+    lse = addr(4) if lse is None else lse
+    return L.ul_attn_fwd_strided(q, k, v, o, lse, 1, N, Hq, Hkv, d, qs, ks, vs, os_, 0.088, 1,
+                                 dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=ctypes.c_void_p(0)), 1),
+    (dict(N=0), 2), (dict(Hq=6, Hkv=4), 3), (dict(d=96), 4),
+    (dict(qs=8 * 128 - 8), 2),            # shorter than the rank's heads
+    (dict(ks=2 * 128 - 1), 2),
+    (dict(os_=(1 << 23) + 8), 2),         # bf16: over 16 MiB per token
+    (dict(qs=W + 4), 5),                  # 8 bytes: not a 16-byte multiple
+    (dict(vs=W + 2, dtype=B.UL_F32), 5),
+    (dict(q=ctypes.c_void_p(A + 8)), 5),
+    # o shares q's stride and starts inside q's first row: same bytes
+    (dict(o=ctypes.c_void_p(A + 64)), 7),
+    # o a head slice that reaches into q's heads of the same buffer
+    (dict(o=ctypes.c_void_p(A + 7 * 256)), 7),
+    # o in the same buffer at a different stride whose span meets q's
+    (dict(o=ctypes.c_void_p(A + 8 * 256), os_=2 * W), 7),
+    # lse inside the span of q's rows
+    (dict(lse=ctypes.c_void_p(A + 100 * W * 2 + 16)), 7),
+])
+def test_fwd_strided_validation(L, kw, code):
+    assert fwd_s(L, **kw) == code
+
+
+def bwd_s(L, strides=None, **kw):
+    p = dict(Bsz=1, N=256, Hq=8, Hkv=2, d=128, scale=0.088, causal=1, dtype=B.UL_BF16)
+    p.update(kw)
+    need = L.ul_attn_bwd_workspace_bytes(p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"], p["dtype"])
+    ptrs = [addr(i) for i in range(9)]
+    for i, n in enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"]):
+        if n in p:
+            ptrs[i] = p.pop(n)
+    ts = [W] * 8 if strides is None else strides
+    return L.ul_attn_bwd_strided(*ptrs, addr(9), need, p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"],
+                                 *ts, p["scale"], p["causal"], p["dtype"], None)
+
+
+PK = (8 + 2 + 2) * 128  # packed [N][Hq + 2 Hkv][128] gradient buffer
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dv=ctypes.c_void_p(0)), 1),
+    (dict(strides=[W, W, W, W, W, W, 255, W]), 2),
+    (dict(strides=[W, W, W, W, W + 4, W, W, W]), 5),
+    # dk's two heads overlap dq's last head inside one packed buffer
+    (dict(dq=ctypes.c_void_p(A + 6 * BIG), dk=ctypes.c_void_p(A + 6 * BIG + 7 * 256),
+          dv=ctypes.c_void_p(A + 6 * BIG + 10 * 256), strides=[W, W, W, W, W, PK, PK, PK]), 7),
+    # dv written over o
+    (dict(dv=ctypes.c_void_p(A + 3 * BIG + 256)), 7),
+])
+def test_bwd_strided_validation(L, kw, code):
+    assert bwd_s(L, **kw) == code
 
 
 @pytest.mark.parametrize("fn", ["ul_relayout_s2h", "ul_relayout_h2s"])

@@ -52,6 +52,9 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_size_t)
         L.ul_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, i32, i32, vp]
         L.ul_attn_fwd.restype = ctypes.c_int
+        L.ul_attn_fwd_strided.argtypes = ([vp] * 5 + [i64, i64, i32, i32, i32] + [i64] * 4 +
+                                          [f32, i32, i32, vp])
+        L.ul_attn_fwd_strided.restype = ctypes.c_int
         L.ul_attn_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
         L.ul_attn_bwd_workspace_bytes.restype = sz
         L.ul_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32,
@@ -59,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.ul_attn_bwd.restype = ctypes.c_int
         L.ul_attn_bwd_stages.argtypes = [i32] + L.ul_attn_bwd.argtypes
         L.ul_attn_bwd_stages.restype = ctypes.c_int
+        L.ul_attn_bwd_strided.argtypes = ([vp] * 10 + [sz, i64, i64, i32, i32, i32] + [i64] * 8 +
+                                          [f32, i32, i32, vp])
+        L.ul_attn_bwd_strided.restype = ctypes.c_int
         for name in ("ul_relayout_s2h", "ul_relayout_h2s"):
             f = getattr(L, name)
             f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
@@ -101,21 +107,42 @@ def _require(t, name: str):
         raise ValueError(f"{name} must be a contiguous device tensor")
 
 
+def _tok_stride(t, name: str) -> int:
+    """Token stride (elements) of a [B, N, H, d] device view whose heads and head dim are
+    dense and whose batches follow each other, as the *_strided calls address it."""
+    if not t.is_cuda or t.dim() != 4:
+        raise ValueError(f"{name} must be a 4-d device tensor")
+    Bn, N, H, d = t.shape
+    if (H > 1 and t.stride(2) != d) or (d > 1 and t.stride(3) != 1):
+        raise ValueError(f"{name}: heads and head dim must be dense")
+    ts = t.stride(1)
+    if Bn > 1 and t.stride(0) != N * ts:
+        raise ValueError(f"{name}: batch stride must be N * token stride")
+    return ts
+
+
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None, lse=None,
              stream=None):
-    """O, lse = attention(q, k, v).  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or fp32)."""
+    """O, lse = attention(q, k, v).  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or fp32).
+
+    q, k, v and `out` may be views with a token stride (for example a rank's head slice
+    of a sequence-sharded [B,N,H,d] tensor); heads and head dim must be dense.
+    """
     import torch
 
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n)
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib().ul_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, N, Hq, Hkv, d,
-                           scale, int(causal), _dtype_code(q), _stream(stream))
-    _check("ul_attn_fwd", st)
+    _require(lse_t, "lse")
+    ts = [_tok_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "out"))]
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, N, Hq, Hkv, d)
+    tail = (scale, int(causal), _dtype_code(q), _stream(stream))
+    if all(t.is_contiguous() for t in (q, k, v, o)):
+        _check("ul_attn_fwd", lib().ul_attn_fwd(*head, *tail))
+    else:
+        _check("ul_attn_fwd_strided", lib().ul_attn_fwd_strided(*head, *ts, *tail))
     return o, lse_t
 
 
@@ -133,8 +160,7 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
     """
     import torch
 
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
-        _require(t, n)
+    _require(lse, "lse")
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -142,16 +168,23 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
     need = workspace_bytes(B, N, Hq, Hkv, d, code)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
-            _ptr(dv), _ptr(workspace), workspace.numel(), B, N, Hq, Hkv, d, scale, int(causal),
-            code, _stream(stream))
-    if stages == UL_BWD_ALL:
-        _check("ul_attn_bwd", lib().ul_attn_bwd(*args))
+    dq = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dv is None else dv
+    tensors = ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+               (dv, "dv"))
+    ts = [_tok_stride(t, n) for t, n in tensors]
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+            _ptr(dv), _ptr(workspace), workspace.numel(), B, N, Hq, Hkv, d)
+    tail = (scale, int(causal), code, _stream(stream))
+    if not all(t.is_contiguous() for t, _ in tensors):
+        if stages != UL_BWD_ALL:
+            raise ValueError("strided tensors run all backward stages")
+        _check("ul_attn_bwd_strided", lib().ul_attn_bwd_strided(*head, *ts, *tail))
+    elif stages == UL_BWD_ALL:
+        _check("ul_attn_bwd", lib().ul_attn_bwd(*head, *tail))
     else:
-        _check("ul_attn_bwd_stages", lib().ul_attn_bwd_stages(int(stages), *args))
+        _check("ul_attn_bwd_stages", lib().ul_attn_bwd_stages(int(stages), *head, *tail))
     return dq, dk, dv
 
 

@@ -41,7 +41,56 @@ Range range(const void *p, int64_t bytes) {
     return Range{lo, lo + (uintptr_t)bytes};
 }
 
+// The kernels address a tile's rows with 32-bit byte offsets (up to 64 rows).
+constexpr int64_t kMaxTokenStrideBytes = int64_t(1) << 24;
+
 bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+int64_t floor_div(int64_t a, int64_t b) {  // b > 0
+    const int64_t q = a / b;
+    return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// The bytes of a tensor: `count` rows of `width` bytes, `stride` bytes apart.
+struct Rows {
+    uintptr_t base;
+    int64_t stride, width, count;
+};
+
+Range span(const Rows &t) { return range(reinterpret_cast<const void *>(t.base), (t.count - 1) * t.stride + t.width); }
+
+// Whether two tensors share a byte.  Rows with the same stride (head slices
+// of one token-major buffer, e.g. q, k and v inside a packed QKV tensor) are
+// compared exactly: row t of a meets row s of b iff, with u = t - s and
+// delta = b.base - a.base,  delta - a.width < u * stride < delta + b.width.
+// Otherwise any intersection of the two spans counts.
+bool intersects(const Rows &a, const Rows &b) {
+    if (!overlap(span(a), span(b))) return false;
+    if (a.stride != b.stride || a.count == 1 || b.count == 1) return true;
+    const int64_t S = a.stride;
+    const int64_t delta = (int64_t)(b.base - a.base);
+    const int64_t u_lo = floor_div(delta - a.width, S) + 1;       // least u: u S > delta - a.width
+    const int64_t u_hi = -floor_div(-(delta + b.width), S) - 1;   // greatest u: u S < delta + b.width
+    const int64_t lo = u_lo > -(b.count - 1) ? u_lo : -(b.count - 1);
+    const int64_t hi = u_hi < a.count - 1 ? u_hi : a.count - 1;
+    return lo <= hi;
+}
+
+// A token-strided attention tensor: B*N tokens of `heads` heads of head_dim
+// elements, `ts` elements from one token to the next.  Fills `rows`.
+ul_status check_tensor(const void *p, int64_t ts, int64_t tokens, int64_t heads, int32_t head_dim,
+                       int64_t es, Rows *rows) {
+    const int64_t width = heads * head_dim;  // elements; both factors validated >= 1
+    if (ts < width || ts > kMaxTokenStrideBytes / es) return UL_ERR_SHAPE;
+    if ((ts * es) % 16 != 0 || !aligned16(p)) return UL_ERR_ALIGNMENT;
+    int64_t last;
+    if (!elems(&last, {tokens - 1, ts, es})) return UL_ERR_SHAPE;
+    if (last > INT64_MAX - width * es) return UL_ERR_SHAPE;
+    *rows = Rows{reinterpret_cast<uintptr_t>(p), ts * es, width * es, tokens};
+    return UL_OK;
+}
+
+Rows dense(const void *p, int64_t bytes) { return Rows{reinterpret_cast<uintptr_t>(p), bytes, bytes, 1}; }
 
 struct AttnSizes {
     int64_t q_bytes, kv_bytes, lse_bytes;
@@ -119,22 +168,33 @@ ul_status ul_relayout_h2s(const void *in, void *out, int64_t C, int64_t N, int32
                                         static_cast<hipStream_t>(stream)));
 }
 
-ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-                      int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                      float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                              int64_t o_tok_stride, float softmax_scale, int32_t causal,
+                              int32_t dtype, void *stream) {
     if (!q || !k || !v || !o || !lse) return UL_ERR_NULL;
     AttnSizes sz;
-    const ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
+    ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return UL_ERR_ALIGNMENT;
-    const Range rq = range(q, sz.q_bytes), rk = range(k, sz.kv_bytes), rv = range(v, sz.kv_bytes);
-    const Range ro = range(o, sz.q_bytes), rl = range(lse, sz.lse_bytes);
-    for (Range out : {ro, rl})
-        for (Range in : {rq, rk, rv})
-            if (overlap(out, in)) return UL_ERR_OVERLAP;
-    if (overlap(ro, rl)) return UL_ERR_OVERLAP;
-    const AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
+    const int64_t es = elt_size(dtype), T = B * N;
+    Rows rq, rk, rv, ro;
+    if ((st = check_tensor(q, q_tok_stride, T, Hq, head_dim, es, &rq)) != UL_OK ||
+        (st = check_tensor(k, k_tok_stride, T, Hkv, head_dim, es, &rk)) != UL_OK ||
+        (st = check_tensor(v, v_tok_stride, T, Hkv, head_dim, es, &rv)) != UL_OK ||
+        (st = check_tensor(o, o_tok_stride, T, Hq, head_dim, es, &ro)) != UL_OK)
+        return st;
+    if (!aligned16(lse)) return UL_ERR_ALIGNMENT;
+    const Rows rl = dense(lse, sz.lse_bytes);
+    for (const Rows &out : {ro, rl})
+        for (const Rows &in : {rq, rk, rv})
+            if (intersects(out, in)) return UL_ERR_OVERLAP;
+    if (intersects(ro, rl)) return UL_ERR_OVERLAP;
+    AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
+    s.q_rs = q_tok_stride;
+    s.k_rs = k_tok_stride;
+    s.v_rs = v_tok_stride;
+    s.o_rs = o_tok_stride;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dtype == UL_F32)
         return from_hip(ul::launch_attn_fwd_f32(static_cast<const float *>(q),
@@ -142,6 +202,14 @@ ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, floa
                                                 static_cast<const float *>(v),
                                                 static_cast<float *>(o), lse, s, hs));
     return from_hip(ul::launch_attn_fwd_bf16(q, k, v, o, lse, s, hs));
+}
+
+ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                      float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    return ul_attn_fwd_strided(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, qs, kvs, kvs, qs,
+                               softmax_scale, causal, dtype, stream);
 }
 
 size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
@@ -152,32 +220,55 @@ size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv
     return ul::attn_bwd_workspace_bytes(s, dtype);
 }
 
-ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const void *v,
-                             const void *o, const void *dout, const float *lse, void *dq, void *dk,
-                             void *dv, void *workspace, size_t workspace_bytes, int64_t B,
-                             int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                             float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+struct BwdStrides {
+    int64_t q, k, v, o, dout, dq, dk, dv;
+};
+
+ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, const void *o,
+                   const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
+                   int32_t Hkv, int32_t head_dim, const BwdStrides &ts, float softmax_scale,
+                   int32_t causal, int32_t dtype, void *stream) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return UL_ERR_NULL;
     AttnSizes sz;
-    const ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
+    ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
     if (stages < 1 || (stages & ~UL_BWD_ALL) != 0) return UL_ERR_UNSUPPORTED;
-    const AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
+    AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
     const size_t need = ul::attn_bwd_workspace_bytes(s, dtype);
     if (!workspace || workspace_bytes < need) return UL_ERR_WORKSPACE;
-    for (const void *ptr : {q, k, v, o, dout, (const void *)lse, (const void *)dq, (const void *)dk,
-                            (const void *)dv, (const void *)workspace})
-        if (!aligned16(ptr)) return UL_ERR_ALIGNMENT;
-    const Range ins[] = {range(q, sz.q_bytes),  range(k, sz.kv_bytes),  range(v, sz.kv_bytes),
-                         range(o, sz.q_bytes),  range(dout, sz.q_bytes), range(lse, sz.lse_bytes)};
-    const Range outs[] = {range(dq, sz.q_bytes), range(dk, sz.kv_bytes), range(dv, sz.kv_bytes),
-                          range(workspace, (int64_t)need)};
+    const int64_t es = elt_size(dtype), T = B * N;
+    Rows r[8];
+    if ((st = check_tensor(q, ts.q, T, Hq, head_dim, es, &r[0])) != UL_OK ||
+        (st = check_tensor(k, ts.k, T, Hkv, head_dim, es, &r[1])) != UL_OK ||
+        (st = check_tensor(v, ts.v, T, Hkv, head_dim, es, &r[2])) != UL_OK ||
+        (st = check_tensor(o, ts.o, T, Hq, head_dim, es, &r[3])) != UL_OK ||
+        (st = check_tensor(dout, ts.dout, T, Hq, head_dim, es, &r[4])) != UL_OK ||
+        (st = check_tensor(dq, ts.dq, T, Hq, head_dim, es, &r[5])) != UL_OK ||
+        (st = check_tensor(dk, ts.dk, T, Hkv, head_dim, es, &r[6])) != UL_OK ||
+        (st = check_tensor(dv, ts.dv, T, Hkv, head_dim, es, &r[7])) != UL_OK)
+        return st;
+    if (!aligned16(lse) || !aligned16(workspace)) return UL_ERR_ALIGNMENT;
+    const Rows ins[] = {r[0], r[1], r[2], r[3], r[4], dense(lse, sz.lse_bytes)};
+    const Rows outs[] = {r[5], r[6], r[7], dense(workspace, (int64_t)need)};
     for (int a = 0; a < 4; ++a) {
-        for (const Range &in : ins)
-            if (overlap(outs[a], in)) return UL_ERR_OVERLAP;
+        for (const Rows &in : ins)
+            if (intersects(outs[a], in)) return UL_ERR_OVERLAP;
         for (int c = a + 1; c < 4; ++c)
-            if (overlap(outs[a], outs[c])) return UL_ERR_OVERLAP;
+            if (intersects(outs[a], outs[c])) return UL_ERR_OVERLAP;
     }
+    s.q_rs = ts.q;
+    s.k_rs = ts.k;
+    s.v_rs = ts.v;
+    s.o_rs = ts.o;
+    s.do_rs = ts.dout;
+    s.dq_rs = ts.dq;
+    s.dk_rs = ts.dk;
+    s.dv_rs = ts.dv;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dtype == UL_F32)
         return from_hip(ul::launch_attn_bwd_f32(
@@ -188,14 +279,47 @@ ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const
     return from_hip(ul::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, s, stages, hs));
 }
 
+BwdStrides dense_strides(int32_t Hq, int32_t Hkv, int32_t head_dim) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    return BwdStrides{qs, kvs, kvs, qs, qs, qs, kvs, kvs};
+}
+
+}  // namespace
+
+extern "C" {
+
+ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const void *v,
+                             const void *o, const void *dout, const float *lse, void *dq, void *dk,
+                             void *dv, void *workspace, size_t workspace_bytes, int64_t B,
+                             int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+    return bwd_impl(stages, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, N,
+                    Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim), softmax_scale, causal,
+                    dtype, stream);
+}
+
 ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, void *dq, void *dk, void *dv,
                       void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
                       int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
                       int32_t dtype, void *stream) {
-    return ul_attn_bwd_stages(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                              workspace_bytes, B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype,
-                              stream);
+    return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                    N, Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim), softmax_scale, causal,
+                    dtype, stream);
+}
+
+ul_status ul_attn_bwd_strided(const void *q, const void *k, const void *v, const void *o,
+                              const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                              void *workspace, size_t workspace_bytes, int64_t B, int64_t N,
+                              int32_t Hq, int32_t Hkv, int32_t head_dim, int64_t q_tok_stride,
+                              int64_t k_tok_stride, int64_t v_tok_stride, int64_t o_tok_stride,
+                              int64_t dout_tok_stride, int64_t dq_tok_stride,
+                              int64_t dk_tok_stride, int64_t dv_tok_stride, float softmax_scale,
+                              int32_t causal, int32_t dtype, void *stream) {
+    const BwdStrides ts{q_tok_stride,    k_tok_stride,  v_tok_stride,  o_tok_stride,
+                        dout_tok_stride, dq_tok_stride, dk_tok_stride, dv_tok_stride};
+    return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                    N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype, stream);
 }
 
 }  // extern "C"

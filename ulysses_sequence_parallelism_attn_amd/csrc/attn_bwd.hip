@@ -45,6 +45,7 @@ struct PreParams {
     const float *lse;
     float *stats;
     int64_t N;
+    int64_t o_rs, do_rs;  // elements between consecutive tokens of o and of dout
     int32_t B, Hq, d;
     int32_t is_bf16;
 };
@@ -57,14 +58,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
     float acc = 0.f;
     if (row < rows) {
         const int per = p.d / 16;
-        const int64_t base = row * p.d + sub * per;
+        // row = (b*N + i)*Hq + h
+        const int64_t tok = row / p.Hq, col = (row % p.Hq) * p.d + sub * per;
+        const int64_t ob = tok * p.o_rs + col, gb = tok * p.do_rs + col;
         if (p.is_bf16) {
-            const uint16_t *o = static_cast<const uint16_t *>(p.o) + base;
-            const uint16_t *g = static_cast<const uint16_t *>(p.dout) + base;
+            const uint16_t *o = static_cast<const uint16_t *>(p.o) + ob;
+            const uint16_t *g = static_cast<const uint16_t *>(p.dout) + gb;
             for (int e = 0; e < per; ++e) acc = fmaf(bf16_to_f32(g[e]), bf16_to_f32(o[e]), acc);
         } else {
-            const float *o = static_cast<const float *>(p.o) + base;
-            const float *g = static_cast<const float *>(p.dout) + base;
+            const float *o = static_cast<const float *>(p.o) + ob;
+            const float *g = static_cast<const float *>(p.dout) + gb;
             for (int e = 0; e < per; ++e) acc = fmaf(g[e], o[e], acc);
         }
     }
@@ -110,6 +113,7 @@ struct DqParams {
     const uint16_t *q, *k, *v, *dout;
     const float *stats;
     uint16_t *dq;
+    int64_t q_rs, k_rs, v_rs, do_rs, dq_rs;  // elements between consecutive tokens of each tensor
     int32_t N, B, Hq, Hkv;
     int32_t heads_per_wg, pos_blocks, head_groups, n_qblk;
     float scale_log2, scale;
@@ -251,9 +255,9 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const int i0 = wg_pos0 + (wave / p.heads_per_wg) * kRowsPerWave;
     const int N = p.N;
     const int row = i0 + m;
-    const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
-    const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
-    const uint16_t *dob = p.dout + ((int64_t)b * N * p.Hq + h) * D;
+    const int64_t q_rs = p.q_rs, do_rs = p.do_rs;
+    const uint16_t *qb = p.q + (int64_t)b * N * q_rs + (int64_t)h * D;
+    const uint16_t *dob = p.dout + (int64_t)b * N * do_rs + (int64_t)h * D;
 
     constexpr int KK = D / 16, EB = D / 32;
     bf16x8 qf[KK], dof[KK];
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     for (int kk = 0; kk < KK; ++kk) {
         qf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(qb + row * q_rs + kk * 16 + kg * 8)
                               : u32x4{0, 0, 0, 0});
-        dof[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + row * q_rs + kk * 16 + kg * 8)
+        dof[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + row * do_rs + kk * 16 + kg * 8)
                                : u32x4{0, 0, 0, 0});
     }
     const int64_t so = ((int64_t)b * p.Hq + h) * 2 * N + (ok ? row : 0);
@@ -310,9 +314,10 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     static_assert((T::kAhead - 1) * kDmaPerWave < 16, "vmcnt immediate");
     const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
     const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
-    const uint16_t *tens = (loads_v ? p.v : p.k) + ((int64_t)b * N * p.Hkv + g) * D;
+    const int64_t t_rs = loads_v ? p.v_rs : p.k_rs;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + (int64_t)b * N * t_rs + (int64_t)g * D;
     const int tile_lds = loads_v ? T::kVBase : 0;
-    const uint32_t row_bytes = (uint32_t)kv_rs * 2;
+    const uint32_t row_bytes = (uint32_t)t_rs * 2;
     uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
@@ -322,7 +327,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
         const int j0 = t * kDqKT;
         const uint32_t lim = (uint32_t)min(N - 1 - j0, kDqKT) * row_bytes;  // last key of the sequence
-        dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
+        dma_b128(tens + (int64_t)j0 * t_rs, min(dma_roff[k], lim) + dma_gran[k],
                  base + tile_lds + (u0 + k) * 1024);
     };
     auto issue = [&](int t, UL_LDS unsigned char *base) {
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 
     // dQ = scale * (dQ^T)^T, rounded to bf16: lane column = query row, registers = head dim
     if (ok) {
-        uint16_t *out = p.dq + ((int64_t)b * N + row) * q_rs + (int64_t)h * D;
+        uint16_t *out = p.dq + ((int64_t)b * N + row) * p.dq_rs + (int64_t)h * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
@@ -445,6 +450,7 @@ struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
     const float *stats;
     uint16_t *dk, *dv;
+    int64_t q_rs, k_rs, v_rs, do_rs, dk_rs, dv_rs;  // elements between consecutive tokens of each tensor
     int32_t N, B, Hq, Hkv;
     int32_t n_kblk;
     float scale_log2, scale;
@@ -623,7 +629,6 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
     const int N = p.N;
-    const int64_t q_rs = (int64_t)p.Hq * D;
     const int kb0 = kblk * kKeysPerWg;
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
@@ -680,8 +685,9 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         bf16x8 kf[KK], vf[KK];
         {
             const bool ok = key < N;
-            const uint16_t *kr = p.k + (((int64_t)b * N + (ok ? key : 0)) * p.Hkv + g) * D;
-            const uint16_t *vr = p.v + (((int64_t)b * N + (ok ? key : 0)) * p.Hkv + g) * D;
+            const int64_t tok = (int64_t)b * N + (ok ? key : 0);
+            const uint16_t *kr = p.k + tok * p.k_rs + (int64_t)g * D;
+            const uint16_t *vr = p.v + tok * p.v_rs + (int64_t)g * D;
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 kf[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(kr + kk * 16 + kg * 8) : u32x4{0, 0, 0, 0});
@@ -753,8 +759,9 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     const bool loads_do = pair * kDmaPerWave >= Tile::INSTR;
     const int u0 = (pair * kDmaPerWave) % Tile::INSTR;
     const uint16_t *tens = loads_do ? p.dout : p.q;
+    const int64_t t_rs = loads_do ? p.do_rs : p.q_rs;
     const int tile_lds = loads_do ? T::kDoBase : 0;
-    const uint32_t row_bytes = (uint32_t)q_rs * 2;
+    const uint32_t row_bytes = (uint32_t)t_rs * 2;
     uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
@@ -768,7 +775,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
         const int h = g * grp + cu.hi;
         if (k < kDmaPerWave) {
-            const uint16_t *tb = tens + (((int64_t)b * N + cu.r0) * p.Hq + h) * D;
+            const uint16_t *tb = tens + ((int64_t)b * N + cu.r0) * t_rs + (int64_t)h * D;
             dma_b128(tb, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
                      lds + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
         } else if (stats_wave) {
@@ -864,8 +871,8 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     for (int k2 = 0; k2 < 2; ++k2) {
         const int key = kb0 + (2 * kh + k2) * kKeysPerWave + m;
         if (key < N) {
-            uint16_t *dkr = p.dk + (((int64_t)b * N + key) * p.Hkv + g) * D;
-            uint16_t *dvr = p.dv + (((int64_t)b * N + key) * p.Hkv + g) * D;
+            uint16_t *dkr = p.dk + ((int64_t)b * N + key) * p.dk_rs + (int64_t)g * D;
+            uint16_t *dvr = p.dv + ((int64_t)b * N + key) * p.dv_rs + (int64_t)g * D;
 #pragma unroll
             for (int e2 = 0; e2 < EBC; ++e2)
 #pragma unroll
@@ -895,6 +902,7 @@ struct BwdF32Params {
     const float *stats;  // the workspace statistics (D is read from it)
     float *dq, *dk, *dv;
     int64_t N;
+    int64_t q_rs, k_rs, v_rs, do_rs, dq_rs, dk_rs, dv_rs;  // token strides in elements
     int32_t B, Hq, Hkv;
     float scale;
     int32_t causal;
@@ -917,8 +925,8 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
     const bool valid = i < N;
     const int64_t ri = valid ? i : 0;
     float qv[D], dov[D], acc[D];
-    const float *qrow = p.q + (((int64_t)b * N + ri) * p.Hq + h) * D;
-    const float *drow = p.dout + (((int64_t)b * N + ri) * p.Hq + h) * D;
+    const float *qrow = p.q + ((int64_t)b * N + ri) * p.q_rs + (int64_t)h * D;
+    const float *drow = p.dout + ((int64_t)b * N + ri) * p.do_rs + (int64_t)h * D;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
         qv[e] = valid ? qrow[e] : 0.f;
@@ -935,9 +943,9 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
         for (int idx = tid; idx < kF32Keys * D; idx += kF32Rows) {
             const int jj = idx / D, e = idx % D;
             const int64_t j = j0 + jj;
-            const int64_t off = (((int64_t)b * N + j) * p.Hkv + g) * D + e;
-            ks[jj][e] = j < N ? p.k[off] : 0.f;
-            vs[jj][e] = j < N ? p.v[off] : 0.f;
+            const int64_t tok = (int64_t)b * N + j, col = (int64_t)g * D + e;
+            ks[jj][e] = j < N ? p.k[tok * p.k_rs + col] : 0.f;
+            vs[jj][e] = j < N ? p.v[tok * p.v_rs + col] : 0.f;
         }
         __syncthreads();
         for (int jj = 0; jj < kF32Keys; ++jj) {
@@ -956,7 +964,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
         }
     }
     if (valid) {
-        float *out = p.dq + (((int64_t)b * N + i) * p.Hq + h) * D;
+        float *out = p.dq + ((int64_t)b * N + i) * p.dq_rs + (int64_t)h * D;
 #pragma unroll
         for (int e = 0; e < D; ++e) out[e] = acc[e] * p.scale;
     }
@@ -983,8 +991,8 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
     const bool valid = j < N;
     const int64_t rj = valid ? j : 0;
     for (int e = 0; e < D; ++e) {
-        kown[tid][e] = valid ? p.k[(((int64_t)b * N + rj) * p.Hkv + g) * D + e] : 0.f;
-        vown[tid][e] = valid ? p.v[(((int64_t)b * N + rj) * p.Hkv + g) * D + e] : 0.f;
+        kown[tid][e] = valid ? p.k[((int64_t)b * N + rj) * p.k_rs + (int64_t)g * D + e] : 0.f;
+        vown[tid][e] = valid ? p.v[((int64_t)b * N + rj) * p.v_rs + (int64_t)g * D + e] : 0.f;
     }
     float dk[D], dv[D];
 #pragma unroll
@@ -998,9 +1006,9 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
             for (int idx = tid; idx < kF32KvRows * D; idx += kF32KvKeys) {
                 const int ii = idx / D, e = idx % D;
                 const int64_t i = i0 + ii;
-                const int64_t off = (((int64_t)b * N + i) * p.Hq + h) * D + e;
-                qs[ii][e] = i < N ? p.q[off] : 0.f;
-                ds_[ii][e] = i < N ? p.dout[off] : 0.f;
+                const int64_t tok = (int64_t)b * N + i, col = (int64_t)h * D + e;
+                qs[ii][e] = i < N ? p.q[tok * p.q_rs + col] : 0.f;
+                ds_[ii][e] = i < N ? p.dout[tok * p.do_rs + col] : 0.f;
             }
             if (tid < kF32KvRows) {
                 const int64_t i = i0 + tid;
@@ -1028,8 +1036,8 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
         }
     }
     if (valid) {
-        float *dkr = p.dk + (((int64_t)b * N + j) * p.Hkv + g) * D;
-        float *dvr = p.dv + (((int64_t)b * N + j) * p.Hkv + g) * D;
+        float *dkr = p.dk + ((int64_t)b * N + j) * p.dk_rs + (int64_t)g * D;
+        float *dvr = p.dv + ((int64_t)b * N + j) * p.dv_rs + (int64_t)g * D;
 #pragma unroll
         for (int e = 0; e < D; ++e) {
             dkr[e] = dk[e] * p.scale;
@@ -1049,7 +1057,7 @@ size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t /*dtype*/) {
 
 static hipError_t launch_pre(const void *o, const void *dout, const float *lse, float *stats,
                              const AttnShape &s, bool bf16, hipStream_t stream) {
-    PreParams pp{o, dout, lse, stats, s.N, (int32_t)s.B, s.Hq, s.d, bf16 ? 1 : 0};
+    PreParams pp{o, dout, lse, stats, s.N, s.o_rs, s.do_rs, (int32_t)s.B, s.Hq, s.d, bf16 ? 1 : 0};
     const int64_t rows = s.B * s.N * s.Hq;
     const int64_t blocks = (rows + 15) / 16;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -1078,6 +1086,11 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     dp.B = (int32_t)s.B;
     dp.Hq = s.Hq;
     dp.Hkv = s.Hkv;
+    dp.q_rs = s.q_rs;
+    dp.k_rs = s.k_rs;
+    dp.v_rs = s.v_rs;
+    dp.do_rs = s.do_rs;
+    dp.dq_rs = s.dq_rs;
     const int grp = s.Hq / s.Hkv;
     dp.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
     dp.pos_blocks = kQWaves / dp.heads_per_wg;
@@ -1102,6 +1115,12 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     kp.B = (int32_t)s.B;
     kp.Hq = s.Hq;
     kp.Hkv = s.Hkv;
+    kp.q_rs = s.q_rs;
+    kp.k_rs = s.k_rs;
+    kp.v_rs = s.v_rs;
+    kp.do_rs = s.do_rs;
+    kp.dk_rs = s.dk_rs;
+    kp.dv_rs = s.dv_rs;
     kp.n_kblk = (int32_t)((s.N + kKeysPerWg - 1) / kKeysPerWg);
     kp.scale_log2 = dp.scale_log2;
     kp.scale = s.scale;
@@ -1146,7 +1165,8 @@ hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, c
         err = launch_pre(o, dout, lse, stats, s, false, stream);
         if (err != hipSuccess) return err;
     }
-    BwdF32Params p{q, k, v, dout, lse, stats, dq, dk, dv, s.N, (int32_t)s.B, s.Hq, s.Hkv,
+    BwdF32Params p{q, k, v, dout, lse, stats, dq, dk, dv, s.N, s.q_rs, s.k_rs, s.v_rs, s.do_rs,
+                   s.dq_rs, s.dk_rs, s.dv_rs, (int32_t)s.B, s.Hq, s.Hkv,
                    s.scale, s.causal, 0};
     p.n_blk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
     const int64_t dq_items = (int64_t)p.n_blk * p.B * p.Hq;

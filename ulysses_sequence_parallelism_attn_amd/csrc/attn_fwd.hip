@@ -61,6 +61,7 @@ struct FwdParams {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
+    int64_t q_rs, k_rs, v_rs, o_rs;  // elements between consecutive tokens of each tensor
     int32_t N, B, Hq, Hkv;
     int32_t heads_per_wg;   // query heads of one KV group handled by one workgroup (1, 2 or 4)
     int32_t pos_blocks;     // 32-position row blocks per workgroup = 8 / heads_per_wg
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const int N = p.N;
     const int row = i0 + m;
 
-    const int64_t q_rs = (int64_t)p.Hq * D, kv_rs = (int64_t)p.Hkv * D;
-    const uint16_t *qb = p.q + ((int64_t)b * N * p.Hq + h) * D;
+    const int64_t q_rs = p.q_rs;
+    const uint16_t *qb = p.q + (int64_t)b * N * q_rs + (int64_t)h * D;
 
     // ---- Q^T fragments (B operand: column = query row, k = head dim)
     constexpr int KK = D / 16, EB = D / 32;
@@ -298,9 +299,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
                   "K and V tiles split evenly over the waves");
     const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
     const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
-    const uint16_t *tens = (loads_v ? p.v : p.k) + ((int64_t)b * N * p.Hkv + g) * D;
+    const int64_t t_rs = loads_v ? p.v_rs : p.k_rs;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + (int64_t)b * N * t_rs + (int64_t)g * D;
     const int tile_lds = loads_v ? T::kVBase : 0;
-    const uint32_t row_bytes = (uint32_t)kv_rs * 2;
+    const uint32_t row_bytes = (uint32_t)t_rs * 2;
     uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
         const int j0 = t * kKT;
         const uint32_t lim = (uint32_t)min(N - 1 - j0, kKT) * row_bytes;  // last key of the sequence
-        dma_b128(tens + (int64_t)j0 * kv_rs, min(dma_roff[k], lim) + dma_gran[k],
+        dma_b128(tens + (int64_t)j0 * t_rs, min(dma_roff[k], lim) + dma_gran[k],
                  base + tile_lds + (u0 + k) * 1024);
     };
     auto issue = [&](int t, UL_LDS unsigned char *base) {
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const float ltot = half_sum(acc.l);
     if (row < N) {
         const float inv = 1.f / ltot;
-        uint16_t *orow = p.o + ((int64_t)b * N + row) * q_rs + (int64_t)h * D;
+        uint16_t *orow = p.o + ((int64_t)b * N + row) * p.o_rs + (int64_t)h * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
@@ -427,6 +429,7 @@ struct FwdF32Params {
     const float *q, *k, *v;
     float *o, *lse;
     int64_t N;
+    int64_t q_rs, k_rs, v_rs, o_rs;  // token strides in elements
     int32_t B, Hq, Hkv;
     float scale;
     int32_t causal;
@@ -449,7 +452,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
     const bool valid = i < N;
 
     float qv[D], acc[D];
-    const float *qrow = p.q + (((int64_t)b * N + (valid ? i : 0)) * p.Hq + h) * D;
+    const float *qrow = p.q + ((int64_t)b * N + (valid ? i : 0)) * p.q_rs + (int64_t)h * D;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
         qv[e] = valid ? qrow[e] : 0.f;
@@ -463,9 +466,9 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
         for (int idx = tid; idx < kF32Keys * D; idx += kF32Rows) {
             const int jj = idx / D, e = idx % D;
             const int64_t j = j0 + jj;
-            const int64_t off = (((int64_t)b * N + j) * p.Hkv + g) * D + e;
-            ks[jj][e] = j < N ? p.k[off] : 0.f;
-            vs[jj][e] = j < N ? p.v[off] : 0.f;
+            const int64_t tok = (int64_t)b * N + j, col = (int64_t)g * D + e;
+            ks[jj][e] = j < N ? p.k[tok * p.k_rs + col] : 0.f;
+            vs[jj][e] = j < N ? p.v[tok * p.v_rs + col] : 0.f;
         }
         __syncthreads();
         for (int jj = 0; jj < kF32Keys; ++jj) {
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
         }
     }
     if (valid) {
-        float *orow = p.o + (((int64_t)b * N + i) * p.Hq + h) * D;
+        float *orow = p.o + ((int64_t)b * N + i) * p.o_rs + (int64_t)h * D;
         const float inv = 1.f / lrow;
 #pragma unroll
         for (int e = 0; e < D; ++e) orow[e] = acc[e] * inv;
@@ -511,6 +514,10 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     p.B = (int32_t)s.B;
     p.Hq = s.Hq;
     p.Hkv = s.Hkv;
+    p.q_rs = s.q_rs;
+    p.k_rs = s.k_rs;
+    p.v_rs = s.v_rs;
+    p.o_rs = s.o_rs;
     const int grp = s.Hq / s.Hkv;
     p.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
     p.pos_blocks = kWaves / p.heads_per_wg;
@@ -536,7 +543,8 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
 
 hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
                                float *lse, const AttnShape &s, hipStream_t stream) {
-    FwdF32Params p{q, k, v, o, lse, s.N, (int32_t)s.B, s.Hq, s.Hkv, s.scale, s.causal, 0};
+    FwdF32Params p{q,      k,      v,      o,      lse,           s.N,  s.q_rs,   s.k_rs,
+                   s.v_rs, s.o_rs, (int32_t)s.B, s.Hq, s.Hkv, s.scale, s.causal, 0};
     p.n_rblk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
     const int64_t items = (int64_t)p.n_rblk * p.B * p.Hq;
     if (items <= 0) return hipSuccess;

@@ -49,11 +49,15 @@ inline hipError_t allow_lds(KernelT kernel, size_t bytes) {
 hipError_t launch_relayout(const void *in, void *out, int64_t C, int64_t N, int64_t H, int64_t d,
                            int64_t P, int64_t elt, bool to_head, hipStream_t stream);
 
+// Sizes of one attention call.  Token t of batch b of a tensor starts
+// (b*N + t) * its token stride elements from the tensor's base pointer; head
+// h of that token starts h*d elements later.
 struct AttnShape {
     int64_t B, N;
     int32_t Hq, Hkv, d;
     float scale;
     int32_t causal;
+    int64_t q_rs, k_rs, v_rs, o_rs, do_rs, dq_rs, dk_rs, dv_rs;  // token strides, elements
 };
 
 hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
