@@ -12,7 +12,8 @@ One step is one pass of the whole path over one batch of synthetic input:
 
 A second measurement, `fused_relayout`, times the same rank's forward and backward through
 the token-strided entry points on sequence-sharded world tensors, i.e. the step with both
-relayouts fused into the attention's own loads and stores.
+relayouts fused into the attention's own loads and stores.  A third, `varlen`, times forward
+and backward over the same 65536 tokens packed as variable-length sequences.
 
 The backward runs as its three C-ABI stages (D/lse preparation, the dQ pass, the dK/dV
 pass) with events between them, so each kernel's duration is measured on the stream it
@@ -188,6 +189,46 @@ def fused_step(B, torch, q, k, v, do, wl, P, args, ms_relayout_path) -> dict:
             "rank": r, "q_tok_stride": views["q"].stride(1), "kv_tok_stride": views["k"].stride(1)}
 
 
+VARLEN_SEED = 3008  # seed of the packed-sequence length mix
+
+
+def varlen_step(B, torch, synth, q, k, v, do, wl, args) -> dict:
+    """Forward and backward over the same 65536 tokens split into packed variable-length
+    sequences (the seeded log-uniform length mix of synth.length_mix), through the varlen
+    entry points.  Counted FLOPs are 7*len^2*Hq*d summed over the sequences."""
+    lengths = synth.length_mix(wl.N, VARLEN_SEED)
+    cu = torch.from_numpy(synth.cu_seqlens(lengths)).to(q.device)
+    mx = int(lengths.max())
+    qv, kv, vv, dov = (t[0] for t in (q, k, v, do))  # [T, H, d], dense
+    o = torch.empty_like(qv)
+    lse = torch.empty((wl.Hq, wl.N), dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty_like(qv), torch.empty_like(kv), torch.empty_like(vv)
+    ws = torch.empty(B.workspace_bytes(1, wl.N, wl.Hq, wl.Hkv, wl.d, B.UL_BF16),
+                     dtype=torch.uint8, device=q.device)
+
+    def step():
+        B.attn_fwd_varlen(qv, kv, vv, cu, mx, wl.scale, True, out=o, lse=lse)
+        B.attn_bwd_varlen(qv, kv, vv, o, dov, lse, cu, mx, wl.scale, True, workspace=ws, dq=dq,
+                          dk=dk, dv=dv)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = float(sum(7.0 * int(n) * int(n) * wl.Hq * wl.d for n in lengths))
+    return {"ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "tokens_per_s": wl.N / (ms * 1e-3), "n_seqs": int(len(lengths)),
+            "max_seqlen": mx, "min_seqlen": int(lengths.min()), "length_mix_seed": VARLEN_SEED,
+            "counted_flop": flops}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +238,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip the strided (relayout-free) variant of the step")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length variant of the step")
     ap.add_argument("--cpu-prefix", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
@@ -366,6 +409,8 @@ def main() -> int:
     }
     if not args.no_fused:
         out["fused_relayout"] = fused_step(B, torch, q, k, v, do, wl, P, args, ms_per_step)
+    if not args.no_varlen:
+        out["varlen"] = varlen_step(B, torch, synth, q, k, v, do, wl, args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, wl, min(args.cpu_prefix, wl.N))
     print(json.dumps(out), flush=True)

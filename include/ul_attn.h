@@ -18,7 +18,8 @@
  *   ul_attn_bwd       its gradient (dQ, dK, dV);
  *   ul_attn_*_strided the same on token-strided views, so that a rank's head
  *                     slice is read from and written to sequence-sharded
- *                     buffers in place (no relayout pass around attention).
+ *                     buffers in place (no relayout pass around attention);
+ *   ul_attn_*_varlen  the same over packed variable-length sequences.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  No call
@@ -123,6 +124,41 @@ ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void 
                               int32_t dtype, void *stream);
 
 /*
+ * ul_attn_fwd over packed variable-length sequences: n_seqs independent
+ * sequences (documents) concatenated along the token axis, each attending
+ * only within itself (causally if `causal`), with no padding between them.
+ * ("Ulysses Sequence Parallelism: Training with Million-Token Contexts":
+ * section "Ulysses vs. Ring Attention: Who's Faster?" makes variable lengths a
+ * mode that has to be switched on; section "Can You Integrate Ulysses with
+ * Hugging Face Today?" asks for bucketed variable-length batches and no
+ * padding.)
+ *
+ *   q, o          [total_tokens][Hq][head_dim]    dtype, dense
+ *   k, v          [total_tokens][Hkv][head_dim]   dtype, dense
+ *   lse           [Hq][total_tokens]              fp32
+ *   cu_seqlens    DEVICE int32 table of n_seqs + 1 token offsets, read by the
+ *                 kernels: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]).
+ *                 It must start at 0, be non-decreasing and end at
+ *                 total_tokens, with no sequence longer than max_seqlen.  The
+ *                 host cannot read it without synchronising, so it is not
+ *                 checked: the kernels clamp every entry into [0, total_tokens]
+ *                 and every length to max_seqlen, so a malformed table gives
+ *                 unspecified values but never an access outside the tensors.
+ *                 Tokens that no sequence covers are left unwritten.  Empty
+ *                 sequences are allowed.
+ *   max_seqlen    the longest sequence (sizes the launch), 1..total_tokens
+ * For each sequence the result is exactly ul_attn_fwd with B = 1 on that
+ * sequence's tokens.  Errors: as ul_attn_fwd (tensor sizes taken with B = 1,
+ * N = total_tokens), plus NULL for cu_seqlens, SHAPE for n_seqs < 1,
+ * max_seqlen outside 1..total_tokens or total_tokens >= 2^31, ALIGNMENT for a
+ * cu_seqlens not 4-byte aligned, and OVERLAP when o or lse overlap the table.
+ */
+ul_status ul_attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                             const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             float softmax_scale, int32_t causal, int32_t dtype, void *stream);
+
+/*
  * Device workspace bytes that ul_attn_bwd needs for these sizes (a multiple
  * of 256).  Returns 0 for invalid sizes.
  */
@@ -197,6 +233,21 @@ ul_status ul_attn_bwd_strided(const void *q, const void *k, const void *v, const
                               int64_t dout_tok_stride, int64_t dq_tok_stride,
                               int64_t dk_tok_stride, int64_t dv_tok_stride, float softmax_scale,
                               int32_t causal, int32_t dtype, void *stream);
+
+/*
+ * Backward of ul_attn_fwd_varlen (all three stages), with its layouts and
+ * table rules: dout and dq [total_tokens][Hq][head_dim], dk and dv
+ * [total_tokens][Hkv][head_dim], o and lse from ul_attn_fwd_varlen for the
+ * same inputs.  The workspace must hold
+ * ul_attn_bwd_workspace_bytes(1, total_tokens, Hq, Hkv, head_dim, dtype)
+ * bytes.  Errors as ul_attn_bwd plus those of ul_attn_fwd_varlen.
+ */
+ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                             const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                             void *workspace, size_t workspace_bytes, const int32_t *cu_seqlens,
+                             int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                             int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                             int32_t dtype, void *stream);
 
 /*
  * Sequence-sharded -> head-sharded relayout (the first all-to-all of the

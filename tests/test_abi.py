@@ -30,10 +30,10 @@ def addr(i):
 
 def test_exports_every_declared_symbol(L):
     names = B.declared_functions()
-    assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_bwd",
-                          "ul_attn_bwd_stages", "ul_attn_bwd_strided",
-                          "ul_attn_bwd_workspace_bytes", "ul_relayout_s2h", "ul_relayout_h2s",
-                          "ul_status_str"}
+    assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_fwd_varlen",
+                          "ul_attn_bwd", "ul_attn_bwd_stages", "ul_attn_bwd_strided",
+                          "ul_attn_bwd_varlen", "ul_attn_bwd_workspace_bytes",
+                          "ul_relayout_s2h", "ul_relayout_h2s", "ul_status_str"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -180,6 +180,58 @@ PK = (8 + 2 + 2) * 128  # packed [N][Hq + 2 Hkv][128] gradient buffer
 ])
 def test_bwd_strided_validation(L, kw, code):
     assert bwd_s(L, **kw) == code
+
+
+# ---- packed variable-length sequences (the table lives at addr(10))
+
+
+def fwd_v(L, q=None, o=None, lse=None, cu=None, n=3, T=1000, max_len=600, Hq=8, Hkv=2, d=128,
+          dtype=B.UL_BF16):
+    q = addr(0) if q is None else q
+    o = addr(3) if o is None else o
+    lse = addr(4) if lse is None else lse
+    cu = addr(10) if cu is None else cu
+    return L.ul_attn_fwd_varlen(q, addr(1), addr(2), o, lse, cu, n, T, max_len, Hq, Hkv, d, 0.088,
+                                1, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=ctypes.c_void_p(0)), 1), (dict(q=ctypes.c_void_p(0)), 1),
+    (dict(n=0), 2), (dict(max_len=0), 2), (dict(max_len=1001), 2), (dict(T=0), 2),
+    (dict(T=1 << 31, max_len=5), 2),
+    (dict(Hq=6, Hkv=4), 3), (dict(d=32), 4),
+    (dict(cu=ctypes.c_void_p(A + 10 * BIG + 2)), 5),
+    (dict(lse=ctypes.c_void_p(A + 10 * BIG)), 7),       # lse over the table
+    (dict(o=ctypes.c_void_p(A + 10 * BIG - 256)), 7),   # o's last row reaches the table
+])
+def test_fwd_varlen_validation(L, kw, code):
+    assert fwd_v(L, **kw) == code
+
+
+def bwd_v(L, ws_bytes=None, n=3, T=1000, max_len=600, **kw):
+    need = L.ul_attn_bwd_workspace_bytes(1, T, 8, 2, 128, B.UL_BF16)
+    ptrs = [addr(i) for i in range(9)]
+    for i, nm in enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv"]):
+        if nm in kw:
+            ptrs[i] = kw.pop(nm)
+    cu = kw.pop("cu", addr(10))
+    return L.ul_attn_bwd_varlen(*ptrs, addr(9), need if ws_bytes is None else ws_bytes, cu, n, T,
+                                max_len, 8, 2, 128, 0.088, 1, B.UL_BF16, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=ctypes.c_void_p(0)), 1), (dict(dv=ctypes.c_void_p(0)), 1),
+    (dict(n=-1), 2), (dict(max_len=2000), 2),
+    (dict(ws_bytes=16), 6),
+    (dict(cu=ctypes.c_void_p(A + 10 * BIG + 1)), 5),
+    (dict(dq=ctypes.c_void_p(A + 10 * BIG - 1024)), 7),  # dq reaches the table
+])
+def test_bwd_varlen_validation(L, kw, code):
+    assert bwd_v(L, **kw) == code
+
+
+def test_varlen_workspace_is_the_single_sequence_size(L):
+    assert L.ul_attn_bwd_workspace_bytes(1, 1000, 8, 2, 128, B.UL_BF16) >= 2 * 8 * 1000 * 4
 
 
 @pytest.mark.parametrize("fn", ["ul_relayout_s2h", "ul_relayout_h2s"])

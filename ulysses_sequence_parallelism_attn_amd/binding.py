@@ -65,6 +65,12 @@ def lib() -> ctypes.CDLL:
         L.ul_attn_bwd_strided.argtypes = ([vp] * 10 + [sz, i64, i64, i32, i32, i32] + [i64] * 8 +
                                           [f32, i32, i32, vp])
         L.ul_attn_bwd_strided.restype = ctypes.c_int
+        L.ul_attn_fwd_varlen.argtypes = ([vp] * 6 + [i32, i64, i32, i32, i32, i32, f32, i32, i32,
+                                                        vp])
+        L.ul_attn_fwd_varlen.restype = ctypes.c_int
+        L.ul_attn_bwd_varlen.argtypes = ([vp] * 10 + [sz, vp, i32, i64, i32, i32, i32, i32, f32, i32,
+                                                        i32, vp])
+        L.ul_attn_bwd_varlen.restype = ctypes.c_int
         for name in ("ul_relayout_s2h", "ul_relayout_h2s"):
             f = getattr(L, name)
             f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
@@ -185,6 +191,68 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
         _check("ul_attn_bwd", lib().ul_attn_bwd(*head, *tail))
     else:
         _check("ul_attn_bwd_stages", lib().ul_attn_bwd_stages(int(stages), *head, *tail))
+    return dq, dk, dv
+
+
+def _require_table(cu):
+    import torch
+
+    if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-d int32 device tensor")
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None,
+                    causal: bool = True, out=None, lse=None, stream=None):
+    """Attention over packed variable-length sequences.
+
+    q [T, Hq, d], k/v [T, Hkv, d] (dense); cu_seqlens: int32 device tensor of the n + 1
+    token offsets; max_seqlen: the longest sequence.  Returns o [T, Hq, d], lse [Hq, T].
+    """
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, n)
+    _require_table(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    o = torch.empty_like(q) if out is None else out
+    lse_t = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, "out")
+    _require(lse_t, "lse")
+    st = lib().ul_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(cu_seqlens),
+                                  cu_seqlens.numel() - 1, T, int(max_seqlen), Hq, Hkv, d, scale,
+                                  int(causal), _dtype_code(q), _stream(stream))
+    _check("ul_attn_fwd_varlen", st)
+    return o, lse_t
+
+
+def attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
+                    scale: float | None = None, causal: bool = True, workspace=None, dq=None,
+                    dk=None, dv=None, stream=None):
+    """dq, dk, dv of L = <dout, attn_fwd_varlen(q, k, v, ...)> (layouts as attn_fwd_varlen)."""
+    import torch
+
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
+        _require(t, n)
+    _require_table(cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    code = _dtype_code(q)
+    need = workspace_bytes(1, T, Hq, Hkv, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _require(t, n)
+    st = lib().ul_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                  _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, int(max_seqlen), Hq,
+                                  Hkv, d, scale, int(causal), code, _stream(stream))
+    _check("ul_attn_bwd_varlen", st)
     return dq, dk, dv
 
 

@@ -168,33 +168,61 @@ ul_status ul_relayout_h2s(const void *in, void *out, int64_t C, int64_t N, int32
                                         static_cast<hipStream_t>(stream)));
 }
 
-ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
-                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                              int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
-                              int64_t o_tok_stride, float softmax_scale, int32_t causal,
-                              int32_t dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Packed variable-length sequences (cu == nullptr: fixed-length batches).
+struct Seqs {
+    const int32_t *cu = nullptr;  // device table of n + 1 token offsets
+    int32_t n = 0, max_len = 0;
+};
+
+// The table is on the device, so only its size and placement are checked
+// here; the kernels clamp its entries (see seq_range).
+ul_status check_seqs(const Seqs &sq, int64_t total) {
+    if (!sq.cu) return UL_ERR_NULL;
+    if (sq.n < 1 || sq.max_len < 1 || sq.max_len > total || total > INT32_MAX) return UL_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(sq.cu) % 4 != 0) return UL_ERR_ALIGNMENT;
+    return UL_OK;
+}
+
+// Tensor extents follow (B, N) and the token strides; with packed sequences
+// B = 1 and N = the total token count.
+ul_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                   int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim, const int64_t ts[4],
+                   float softmax_scale, int32_t causal, int32_t dtype, void *stream,
+                   const Seqs *seqs) {
     if (!q || !k || !v || !o || !lse) return UL_ERR_NULL;
     AttnSizes sz;
     ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
+    if (seqs && (st = check_seqs(*seqs, N)) != UL_OK) return st;
     const int64_t es = elt_size(dtype), T = B * N;
     Rows rq, rk, rv, ro;
-    if ((st = check_tensor(q, q_tok_stride, T, Hq, head_dim, es, &rq)) != UL_OK ||
-        (st = check_tensor(k, k_tok_stride, T, Hkv, head_dim, es, &rk)) != UL_OK ||
-        (st = check_tensor(v, v_tok_stride, T, Hkv, head_dim, es, &rv)) != UL_OK ||
-        (st = check_tensor(o, o_tok_stride, T, Hq, head_dim, es, &ro)) != UL_OK)
+    if ((st = check_tensor(q, ts[0], T, Hq, head_dim, es, &rq)) != UL_OK ||
+        (st = check_tensor(k, ts[1], T, Hkv, head_dim, es, &rk)) != UL_OK ||
+        (st = check_tensor(v, ts[2], T, Hkv, head_dim, es, &rv)) != UL_OK ||
+        (st = check_tensor(o, ts[3], T, Hq, head_dim, es, &ro)) != UL_OK)
         return st;
     if (!aligned16(lse)) return UL_ERR_ALIGNMENT;
     const Rows rl = dense(lse, sz.lse_bytes);
+    const Rows rc = seqs ? dense(seqs->cu, ((int64_t)seqs->n + 1) * 4) : dense(nullptr, 0);
     for (const Rows &out : {ro, rl})
-        for (const Rows &in : {rq, rk, rv})
+        for (const Rows &in : {rq, rk, rv, rc})
             if (intersects(out, in)) return UL_ERR_OVERLAP;
     if (intersects(ro, rl)) return UL_ERR_OVERLAP;
     AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
-    s.q_rs = q_tok_stride;
-    s.k_rs = k_tok_stride;
-    s.v_rs = v_tok_stride;
-    s.o_rs = o_tok_stride;
+    s.q_rs = ts[0];
+    s.k_rs = ts[1];
+    s.v_rs = ts[2];
+    s.o_rs = ts[3];
+    if (seqs) {
+        s.B = seqs->n;
+        s.N = seqs->max_len;
+        s.cu = seqs->cu;
+        s.total = N;
+    }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dtype == UL_F32)
         return from_hip(ul::launch_attn_fwd_f32(static_cast<const float *>(q),
@@ -204,42 +232,28 @@ ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void 
     return from_hip(ul::launch_attn_fwd_bf16(q, k, v, o, lse, s, hs));
 }
 
-ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
-                      int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
-                      float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
-    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
-    return ul_attn_fwd_strided(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, qs, kvs, kvs, qs,
-                               softmax_scale, causal, dtype, stream);
-}
-
-size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
-                                   int32_t head_dim, int32_t dtype) {
-    AttnSizes sz;
-    if (check_attn(B, N, Hq, Hkv, head_dim, 1.0f, 1, dtype, &sz) != UL_OK) return 0;
-    const AttnShape s{B, N, Hq, Hkv, head_dim, 1.0f, 1};
-    return ul::attn_bwd_workspace_bytes(s, dtype);
-}
-
-}  // extern "C"
-
-namespace {
-
 struct BwdStrides {
     int64_t q, k, v, o, dout, dq, dk, dv;
 };
+
+BwdStrides dense_strides(int32_t Hq, int32_t Hkv, int32_t head_dim) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    return BwdStrides{qs, kvs, kvs, qs, qs, qs, kvs, kvs};
+}
 
 ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, const void *o,
                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
                    void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
                    int32_t Hkv, int32_t head_dim, const BwdStrides &ts, float softmax_scale,
-                   int32_t causal, int32_t dtype, void *stream) {
+                   int32_t causal, int32_t dtype, void *stream, const Seqs *seqs) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return UL_ERR_NULL;
     AttnSizes sz;
     ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
+    if (seqs && (st = check_seqs(*seqs, N)) != UL_OK) return st;
     if (stages < 1 || (stages & ~UL_BWD_ALL) != 0) return UL_ERR_UNSUPPORTED;
     AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
-    const size_t need = ul::attn_bwd_workspace_bytes(s, dtype);
+    const size_t need = ul::attn_bwd_workspace_bytes(s, dtype);  // packed: B = 1, N = total
     if (!workspace || workspace_bytes < need) return UL_ERR_WORKSPACE;
     const int64_t es = elt_size(dtype), T = B * N;
     Rows r[8];
@@ -253,7 +267,8 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
         (st = check_tensor(dv, ts.dv, T, Hkv, head_dim, es, &r[7])) != UL_OK)
         return st;
     if (!aligned16(lse) || !aligned16(workspace)) return UL_ERR_ALIGNMENT;
-    const Rows ins[] = {r[0], r[1], r[2], r[3], r[4], dense(lse, sz.lse_bytes)};
+    const Rows ins[] = {r[0], r[1], r[2], r[3], r[4], dense(lse, sz.lse_bytes),
+                        seqs ? dense(seqs->cu, ((int64_t)seqs->n + 1) * 4) : dense(nullptr, 0)};
     const Rows outs[] = {r[5], r[6], r[7], dense(workspace, (int64_t)need)};
     for (int a = 0; a < 4; ++a) {
         for (const Rows &in : ins)
@@ -269,6 +284,12 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
     s.dq_rs = ts.dq;
     s.dk_rs = ts.dk;
     s.dv_rs = ts.dv;
+    if (seqs) {
+        s.B = seqs->n;
+        s.N = seqs->max_len;
+        s.cu = seqs->cu;
+        s.total = N;
+    }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dtype == UL_F32)
         return from_hip(ul::launch_attn_bwd_f32(
@@ -279,14 +300,50 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
     return from_hip(ul::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, workspace, s, stages, hs));
 }
 
-BwdStrides dense_strides(int32_t Hq, int32_t Hkv, int32_t head_dim) {
-    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
-    return BwdStrides{qs, kvs, kvs, qs, qs, qs, kvs, kvs};
-}
-
 }  // namespace
 
 extern "C" {
+
+ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              int64_t q_tok_stride, int64_t k_tok_stride, int64_t v_tok_stride,
+                              int64_t o_tok_stride, float softmax_scale, int32_t causal,
+                              int32_t dtype, void *stream) {
+    const int64_t ts[4] = {q_tok_stride, k_tok_stride, v_tok_stride, o_tok_stride};
+    return fwd_impl(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype,
+                    stream, nullptr);
+}
+
+ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                      int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                      float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    const int64_t ts[4] = {qs, kvs, kvs, qs};
+    return fwd_impl(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype,
+                    stream, nullptr);
+}
+
+ul_status ul_attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                             const int32_t *cu_seqlens, int32_t n_seqs, int64_t total_tokens,
+                             int32_t max_seqlen, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                             float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    const int64_t ts[4] = {qs, kvs, kvs, qs};
+    Seqs sq;
+    sq.cu = cu_seqlens;
+    sq.n = n_seqs;
+    sq.max_len = max_seqlen;
+    return fwd_impl(q, k, v, o, lse, 1, total_tokens, Hq, Hkv, head_dim, ts, softmax_scale, causal,
+                    dtype, stream, &sq);
+}
+
+size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t dtype) {
+    AttnSizes sz;
+    if (check_attn(B, N, Hq, Hkv, head_dim, 1.0f, 1, dtype, &sz) != UL_OK) return 0;
+    const AttnShape s{B, N, Hq, Hkv, head_dim, 1.0f, 1};
+    return ul::attn_bwd_workspace_bytes(s, dtype);
+}
 
 ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const void *v,
                              const void *o, const void *dout, const float *lse, void *dq, void *dk,
@@ -295,7 +352,7 @@ ul_status ul_attn_bwd_stages(int32_t stages, const void *q, const void *k, const
                              float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
     return bwd_impl(stages, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, N,
                     Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim), softmax_scale, causal,
-                    dtype, stream);
+                    dtype, stream, nullptr);
 }
 
 ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
@@ -305,7 +362,7 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
                       int32_t dtype, void *stream) {
     return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
                     N, Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim), softmax_scale, causal,
-                    dtype, stream);
+                    dtype, stream, nullptr);
 }
 
 ul_status ul_attn_bwd_strided(const void *q, const void *k, const void *v, const void *o,
@@ -319,7 +376,22 @@ ul_status ul_attn_bwd_strided(const void *q, const void *k, const void *v, const
     const BwdStrides ts{q_tok_stride,    k_tok_stride,  v_tok_stride,  o_tok_stride,
                         dout_tok_stride, dq_tok_stride, dk_tok_stride, dv_tok_stride};
     return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
-                    N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype, stream);
+                    N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype, stream, nullptr);
+}
+
+ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                             const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                             void *workspace, size_t workspace_bytes, const int32_t *cu_seqlens,
+                             int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
+                             int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                             int32_t dtype, void *stream) {
+    Seqs sq;
+    sq.cu = cu_seqlens;
+    sq.n = n_seqs;
+    sq.max_len = max_seqlen;
+    return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, 1,
+                    total_tokens, Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim),
+                    softmax_scale, causal, dtype, stream, &sq);
 }
 
 }  // extern "C"

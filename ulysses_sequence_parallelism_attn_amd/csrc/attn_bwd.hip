@@ -114,7 +114,9 @@ struct DqParams {
     const float *stats;
     uint16_t *dq;
     int64_t q_rs, k_rs, v_rs, do_rs, dq_rs;  // elements between consecutive tokens of each tensor
-    int32_t N, B, Hq, Hkv;
+    const int32_t *cu_seqlens;  // packed variable-length sequences, or nullptr
+    int64_t total;              // tokens of the packed sequences
+    int32_t N, B, Hq, Hkv;      // N: tokens per sequence (the longest one if packed)
     int32_t heads_per_wg, pos_blocks, head_groups, n_qblk;
     float scale_log2, scale;
     int32_t causal;
@@ -253,11 +255,13 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const int wg_rows = kRowsPerWave * p.pos_blocks;
     const int wg_pos0 = qblk * wg_rows;
     const int i0 = wg_pos0 + (wave / p.heads_per_wg) * kRowsPerWave;
-    const int N = p.N;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
+    const int N = sq.len;
     const int row = i0 + m;
+    if (wg_pos0 >= N) return;  // past the end of a shorter packed sequence
     const int64_t q_rs = p.q_rs, do_rs = p.do_rs;
-    const uint16_t *qb = p.q + (int64_t)b * N * q_rs + (int64_t)h * D;
-    const uint16_t *dob = p.dout + (int64_t)b * N * do_rs + (int64_t)h * D;
+    const uint16_t *qb = p.q + sq.tok0 * q_rs + (int64_t)h * D;
+    const uint16_t *dob = p.dout + sq.tok0 * do_rs + (int64_t)h * D;
 
     constexpr int KK = D / 16, EB = D / 32;
     bf16x8 qf[KK], dof[KK];
@@ -269,9 +273,9 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
         dof[kk] = as_bf16x8(ok ? *reinterpret_cast<const u32x4 *>(dob + row * do_rs + kk * 16 + kg * 8)
                                : u32x4{0, 0, 0, 0});
     }
-    const int64_t so = ((int64_t)b * p.Hq + h) * 2 * N + (ok ? row : 0);
+    const int64_t so = sq.st0 + (int64_t)h * 2 * sq.hs + (ok ? row : 0);
     const float lse2 = ok ? p.stats[so] : 0.f;
-    const float Drow = ok ? p.stats[so + N] : 0.f;
+    const float Drow = ok ? p.stats[so + sq.hs] : 0.f;
     // Retire these loads: inside the loop vmcnt counts only the tile loads.
     __builtin_amdgcn_s_waitcnt(0x70);
 
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
     const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
     const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
     const int64_t t_rs = loads_v ? p.v_rs : p.k_rs;
-    const uint16_t *tens = (loads_v ? p.v : p.k) + (int64_t)b * N * t_rs + (int64_t)g * D;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + sq.tok0 * t_rs + (int64_t)g * D;
     const int tile_lds = loads_v ? T::kVBase : 0;
     const uint32_t row_bytes = (uint32_t)t_rs * 2;
     uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 
     // dQ = scale * (dQ^T)^T, rounded to bf16: lane column = query row, registers = head dim
     if (ok) {
-        uint16_t *out = p.dq + ((int64_t)b * N + row) * p.dq_rs + (int64_t)h * D;
+        uint16_t *out = p.dq + (sq.tok0 + row) * p.dq_rs + (int64_t)h * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
@@ -451,7 +455,9 @@ struct DkvParams {
     const float *stats;
     uint16_t *dk, *dv;
     int64_t q_rs, k_rs, v_rs, do_rs, dk_rs, dv_rs;  // elements between consecutive tokens of each tensor
-    int32_t N, B, Hq, Hkv;
+    const int32_t *cu_seqlens;  // packed variable-length sequences, or nullptr
+    int64_t total;              // tokens of the packed sequences
+    int32_t N, B, Hq, Hkv;      // N: tokens per sequence (the longest one if packed)
     int32_t n_kblk;
     float scale_log2, scale;
     int32_t causal;
@@ -628,8 +634,10 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     const int bg = blockIdx.x - kblk * per_rank;
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
-    const int N = p.N;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
+    const int N = sq.len;
     const int kb0 = kblk * kKeysPerWg;
+    if (kb0 >= N) return;  // past the end of a shorter packed sequence
     const uint32_t lbase = (uint32_t)(uintptr_t)lds;
 
     // Steps: 32-row tiles from the end of the sequence down to the causal
@@ -685,7 +693,7 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         bf16x8 kf[KK], vf[KK];
         {
             const bool ok = key < N;
-            const int64_t tok = (int64_t)b * N + (ok ? key : 0);
+            const int64_t tok = sq.tok0 + (ok ? key : 0);
             const uint16_t *kr = p.k + tok * p.k_rs + (int64_t)g * D;
             const uint16_t *vr = p.v + tok * p.v_rs + (int64_t)g * D;
 #pragma unroll
@@ -775,18 +783,19 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
         const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
         const int h = g * grp + cu.hi;
         if (k < kDmaPerWave) {
-            const uint16_t *tb = tens + ((int64_t)b * N + cu.r0) * t_rs + (int64_t)h * D;
+            const uint16_t *tb = tens + (sq.tok0 + cu.r0) * t_rs + (int64_t)h * D;
             dma_b128(tb, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
                      lds + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
         } else if (stats_wave) {
-            // lanes 0..31 read the lse2 rows, lanes 32..63 the D rows N floats
-            // later (each lane lands at its own dword of the stage's block)
-            const float *sl = p.stats + ((int64_t)b * p.Hq + h) * 2 * N + cu.r0;
+            // lanes 0..31 read the lse2 rows, lanes 32..63 the D rows one
+            // statistics block later (each lane lands at its own dword of the
+            // stage's block)
+            const float *sl = p.stats + sq.st0 + (int64_t)h * 2 * sq.hs + cu.r0;
             const int r = min(lane & (kQT - 1), lim);
             if (lane < kQT)
                 dma_b32(sl, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
             else
-                dma_b32(sl + N, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
+                dma_b32(sl + sq.hs, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
         }
     };
     auto issue = [&](const Cur &cu, int st) {
@@ -871,8 +880,8 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     for (int k2 = 0; k2 < 2; ++k2) {
         const int key = kb0 + (2 * kh + k2) * kKeysPerWave + m;
         if (key < N) {
-            uint16_t *dkr = p.dk + ((int64_t)b * N + key) * p.dk_rs + (int64_t)g * D;
-            uint16_t *dvr = p.dv + ((int64_t)b * N + key) * p.dv_rs + (int64_t)g * D;
+            uint16_t *dkr = p.dk + (sq.tok0 + key) * p.dk_rs + (int64_t)g * D;
+            uint16_t *dvr = p.dv + (sq.tok0 + key) * p.dv_rs + (int64_t)g * D;
 #pragma unroll
             for (int e2 = 0; e2 < EBC; ++e2)
 #pragma unroll
@@ -903,6 +912,8 @@ struct BwdF32Params {
     float *dq, *dk, *dv;
     int64_t N;
     int64_t q_rs, k_rs, v_rs, do_rs, dq_rs, dk_rs, dv_rs;  // token strides in elements
+    const int32_t *cu_seqlens;  // packed variable-length sequences, or nullptr
+    int64_t total;
     int32_t B, Hq, Hkv;
     float scale;
     int32_t causal;
@@ -920,22 +931,23 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
     const int rblk = p.causal ? (p.n_blk - 1 - rank) : rank;
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int g = h / (p.Hq / p.Hkv);
-    const int64_t N = p.N;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
+    const int64_t N = sq.len;
+    if ((int64_t)rblk * kF32Rows >= N) return;  // past the end of a shorter packed sequence
     const int64_t i = (int64_t)rblk * kF32Rows + tid;
     const bool valid = i < N;
     const int64_t ri = valid ? i : 0;
     float qv[D], dov[D], acc[D];
-    const float *qrow = p.q + ((int64_t)b * N + ri) * p.q_rs + (int64_t)h * D;
-    const float *drow = p.dout + ((int64_t)b * N + ri) * p.do_rs + (int64_t)h * D;
+    const float *qrow = p.q + (sq.tok0 + ri) * p.q_rs + (int64_t)h * D;
+    const float *drow = p.dout + (sq.tok0 + ri) * p.do_rs + (int64_t)h * D;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
         qv[e] = valid ? qrow[e] : 0.f;
         dov[e] = valid ? drow[e] : 0.f;
         acc[e] = 0.f;
     }
-    const int64_t so = ((int64_t)b * p.Hq + h) * N + ri;
-    const float lse = valid ? p.lse[so] : 0.f;
-    const float Di = valid ? p.stats[so + ((int64_t)b * p.Hq + h + 1) * N] : 0.f;
+    const float lse = valid ? p.lse[sq.lse0 + (int64_t)h * sq.hs + ri] : 0.f;
+    const float Di = valid ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + ri] : 0.f;
     const int64_t blk_last = (int64_t)rblk * kF32Rows + kF32Rows - 1;
     const int64_t kend = p.causal ? (blk_last + 1 < N ? blk_last + 1 : N) : N;
     for (int64_t j0 = 0; j0 < kend; j0 += kF32Keys) {
@@ -943,7 +955,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
         for (int idx = tid; idx < kF32Keys * D; idx += kF32Rows) {
             const int jj = idx / D, e = idx % D;
             const int64_t j = j0 + jj;
-            const int64_t tok = (int64_t)b * N + j, col = (int64_t)g * D + e;
+            const int64_t tok = sq.tok0 + j, col = (int64_t)g * D + e;
             ks[jj][e] = j < N ? p.k[tok * p.k_rs + col] : 0.f;
             vs[jj][e] = j < N ? p.v[tok * p.v_rs + col] : 0.f;
         }
@@ -964,7 +976,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
         }
     }
     if (valid) {
-        float *out = p.dq + ((int64_t)b * N + i) * p.dq_rs + (int64_t)h * D;
+        float *out = p.dq + (sq.tok0 + i) * p.dq_rs + (int64_t)h * D;
 #pragma unroll
         for (int e = 0; e < D; ++e) out[e] = acc[e] * p.scale;
     }
@@ -986,13 +998,15 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
     const int kblk = blockIdx.x / (p.B * p.Hkv);
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
-    const int64_t N = p.N;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
+    const int64_t N = sq.len;
+    if ((int64_t)kblk * kF32KvKeys >= N) return;  // past the end of a shorter packed sequence
     const int64_t j = (int64_t)kblk * kF32KvKeys + tid;
     const bool valid = j < N;
     const int64_t rj = valid ? j : 0;
     for (int e = 0; e < D; ++e) {
-        kown[tid][e] = valid ? p.k[((int64_t)b * N + rj) * p.k_rs + (int64_t)g * D + e] : 0.f;
-        vown[tid][e] = valid ? p.v[((int64_t)b * N + rj) * p.v_rs + (int64_t)g * D + e] : 0.f;
+        kown[tid][e] = valid ? p.k[(sq.tok0 + rj) * p.k_rs + (int64_t)g * D + e] : 0.f;
+        vown[tid][e] = valid ? p.v[(sq.tok0 + rj) * p.v_rs + (int64_t)g * D + e] : 0.f;
     }
     float dk[D], dv[D];
 #pragma unroll
@@ -1006,15 +1020,14 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
             for (int idx = tid; idx < kF32KvRows * D; idx += kF32KvKeys) {
                 const int ii = idx / D, e = idx % D;
                 const int64_t i = i0 + ii;
-                const int64_t tok = (int64_t)b * N + i, col = (int64_t)h * D + e;
+                const int64_t tok = sq.tok0 + i, col = (int64_t)h * D + e;
                 qs[ii][e] = i < N ? p.q[tok * p.q_rs + col] : 0.f;
                 ds_[ii][e] = i < N ? p.dout[tok * p.do_rs + col] : 0.f;
             }
             if (tid < kF32KvRows) {
                 const int64_t i = i0 + tid;
-                const int64_t so = ((int64_t)b * p.Hq + h) * N + i;
-                ls[tid] = i < N ? p.lse[so] : 0.f;
-                Ds[tid] = i < N ? p.stats[so + ((int64_t)b * p.Hq + h + 1) * N] : 0.f;
+                ls[tid] = i < N ? p.lse[sq.lse0 + (int64_t)h * sq.hs + i] : 0.f;
+                Ds[tid] = i < N ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + i] : 0.f;
             }
             __syncthreads();
             for (int ii = 0; ii < kF32KvRows; ++ii) {
@@ -1036,8 +1049,8 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
         }
     }
     if (valid) {
-        float *dkr = p.dk + ((int64_t)b * N + j) * p.dk_rs + (int64_t)g * D;
-        float *dvr = p.dv + ((int64_t)b * N + j) * p.dv_rs + (int64_t)g * D;
+        float *dkr = p.dk + (sq.tok0 + j) * p.dk_rs + (int64_t)g * D;
+        float *dvr = p.dv + (sq.tok0 + j) * p.dv_rs + (int64_t)g * D;
 #pragma unroll
         for (int e = 0; e < D; ++e) {
             dkr[e] = dk[e] * p.scale;
@@ -1051,14 +1064,17 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t /*dtype*/) {
-    const size_t rows = (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
+    const size_t rows = s.cu ? (size_t)s.Hq * (size_t)s.total : (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
     return round256(2 * rows * sizeof(float));
 }
 
 static hipError_t launch_pre(const void *o, const void *dout, const float *lse, float *stats,
                              const AttnShape &s, bool bf16, hipStream_t stream) {
-    PreParams pp{o, dout, lse, stats, s.N, s.o_rs, s.do_rs, (int32_t)s.B, s.Hq, s.d, bf16 ? 1 : 0};
-    const int64_t rows = s.B * s.N * s.Hq;
+    // Packed sequences lay lse and the statistics out as one sequence of
+    // `total` tokens, so the pre-pass runs over all of them at once.
+    const int64_t Bp = s.cu ? 1 : s.B, Np = s.cu ? s.total : s.N;
+    PreParams pp{o, dout, lse, stats, Np, s.o_rs, s.do_rs, (int32_t)Bp, s.Hq, s.d, bf16 ? 1 : 0};
+    const int64_t rows = Bp * Np * s.Hq;
     const int64_t blocks = (rows + 15) / 16;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, pp);
@@ -1091,6 +1107,8 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     dp.v_rs = s.v_rs;
     dp.do_rs = s.do_rs;
     dp.dq_rs = s.dq_rs;
+    dp.cu_seqlens = s.cu;
+    dp.total = s.total;
     const int grp = s.Hq / s.Hkv;
     dp.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
     dp.pos_blocks = kQWaves / dp.heads_per_wg;
@@ -1121,6 +1139,8 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     kp.do_rs = s.do_rs;
     kp.dk_rs = s.dk_rs;
     kp.dv_rs = s.dv_rs;
+    kp.cu_seqlens = s.cu;
+    kp.total = s.total;
     kp.n_kblk = (int32_t)((s.N + kKeysPerWg - 1) / kKeysPerWg);
     kp.scale_log2 = dp.scale_log2;
     kp.scale = s.scale;
@@ -1166,7 +1186,7 @@ hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, c
         if (err != hipSuccess) return err;
     }
     BwdF32Params p{q, k, v, dout, lse, stats, dq, dk, dv, s.N, s.q_rs, s.k_rs, s.v_rs, s.do_rs,
-                   s.dq_rs, s.dk_rs, s.dv_rs, (int32_t)s.B, s.Hq, s.Hkv,
+                   s.dq_rs, s.dk_rs, s.dv_rs, s.cu, s.total, (int32_t)s.B, s.Hq, s.Hkv,
                    s.scale, s.causal, 0};
     p.n_blk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
     const int64_t dq_items = (int64_t)p.n_blk * p.B * p.Hq;

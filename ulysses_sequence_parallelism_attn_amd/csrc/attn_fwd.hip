@@ -62,7 +62,9 @@ struct FwdParams {
     uint16_t *o;
     float *lse;
     int64_t q_rs, k_rs, v_rs, o_rs;  // elements between consecutive tokens of each tensor
-    int32_t N, B, Hq, Hkv;
+    const int32_t *cu_seqlens;       // packed variable-length sequences, or nullptr
+    int64_t total;                   // tokens of the packed sequences
+    int32_t N, B, Hq, Hkv;           // N: tokens per sequence (the longest one if packed)
     int32_t heads_per_wg;   // query heads of one KV group handled by one workgroup (1, 2 or 4)
     int32_t pos_blocks;     // 32-position row blocks per workgroup = 8 / heads_per_wg
     int32_t head_groups;    // (Hq/Hkv) / heads_per_wg
@@ -238,17 +240,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const int hg = rest % p.head_groups;
     const int b = rest / p.head_groups;
     const int qblk = p.causal ? (p.n_qblk - 1 - rank) : rank;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
 
     const int grp = p.Hq / p.Hkv;
     const int h = g * grp + hg * p.heads_per_wg + (wave % p.heads_per_wg);
     const int wg_rows = kRowsPerWave * p.pos_blocks;
     const int wg_pos0 = qblk * wg_rows;
     const int i0 = wg_pos0 + (wave / p.heads_per_wg) * kRowsPerWave;
-    const int N = p.N;
+    const int N = sq.len;
     const int row = i0 + m;
+    if (wg_pos0 >= N) return;  // past the end of a shorter packed sequence
 
     const int64_t q_rs = p.q_rs;
-    const uint16_t *qb = p.q + (int64_t)b * N * q_rs + (int64_t)h * D;
+    const uint16_t *qb = p.q + sq.tok0 * q_rs + (int64_t)h * D;
 
     // ---- Q^T fragments (B operand: column = query row, k = head dim)
     constexpr int KK = D / 16, EB = D / 32;
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const bool loads_v = wave * kDmaPerWave >= Tile::INSTR;
     const int u0 = (wave * kDmaPerWave) % Tile::INSTR;
     const int64_t t_rs = loads_v ? p.v_rs : p.k_rs;
-    const uint16_t *tens = (loads_v ? p.v : p.k) + (int64_t)b * N * t_rs + (int64_t)g * D;
+    const uint16_t *tens = (loads_v ? p.v : p.k) + sq.tok0 * t_rs + (int64_t)g * D;
     const int tile_lds = loads_v ? T::kVBase : 0;
     const uint32_t row_bytes = (uint32_t)t_rs * 2;
     uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     const float ltot = half_sum(acc.l);
     if (row < N) {
         const float inv = 1.f / ltot;
-        uint16_t *orow = p.o + ((int64_t)b * N + row) * p.o_rs + (int64_t)h * D;
+        uint16_t *orow = p.o + (sq.tok0 + row) * p.o_rs + (int64_t)h * D;
 #pragma unroll
         for (int eb = 0; eb < EB; ++eb)
 #pragma unroll
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
                 for (int q = 0; q < 4; ++q) ov[q] = (__bf16)(acc.o[eb][r4 * 4 + q] * inv);
                 *reinterpret_cast<u32x2 *>(orow + eb * 32 + r4 * 8 + kg * 4) = __builtin_bit_cast(u32x2, ov);
             }
-        if (kg == 0) p.lse[((int64_t)b * p.Hq + h) * N + row] = (acc.m + __log2f(ltot)) * kLn2;
+        if (kg == 0) p.lse[sq.lse0 + (int64_t)h * sq.hs + row] = (acc.m + __log2f(ltot)) * kLn2;
     }
 }
 
@@ -430,6 +434,8 @@ struct FwdF32Params {
     float *o, *lse;
     int64_t N;
     int64_t q_rs, k_rs, v_rs, o_rs;  // token strides in elements
+    const int32_t *cu_seqlens;       // packed variable-length sequences, or nullptr
+    int64_t total;
     int32_t B, Hq, Hkv;
     float scale;
     int32_t causal;
@@ -447,12 +453,14 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
     const int rblk = p.causal ? (p.n_rblk - 1 - rank) : rank;
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int g = h / (p.Hq / p.Hkv);
-    const int64_t N = p.N;
+    const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
+    const int64_t N = sq.len;
+    if ((int64_t)rblk * kF32Rows >= N) return;  // past the end of a shorter packed sequence
     const int64_t i = (int64_t)rblk * kF32Rows + tid;
     const bool valid = i < N;
 
     float qv[D], acc[D];
-    const float *qrow = p.q + ((int64_t)b * N + (valid ? i : 0)) * p.q_rs + (int64_t)h * D;
+    const float *qrow = p.q + (sq.tok0 + (valid ? i : 0)) * p.q_rs + (int64_t)h * D;
 #pragma unroll
     for (int e = 0; e < D; ++e) {
         qv[e] = valid ? qrow[e] : 0.f;
@@ -466,7 +474,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
         for (int idx = tid; idx < kF32Keys * D; idx += kF32Rows) {
             const int jj = idx / D, e = idx % D;
             const int64_t j = j0 + jj;
-            const int64_t tok = (int64_t)b * N + j, col = (int64_t)g * D + e;
+            const int64_t tok = sq.tok0 + j, col = (int64_t)g * D + e;
             ks[jj][e] = j < N ? p.k[tok * p.k_rs + col] : 0.f;
             vs[jj][e] = j < N ? p.v[tok * p.v_rs + col] : 0.f;
         }
@@ -492,11 +500,11 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
         }
     }
     if (valid) {
-        float *orow = p.o + ((int64_t)b * N + i) * p.o_rs + (int64_t)h * D;
+        float *orow = p.o + (sq.tok0 + i) * p.o_rs + (int64_t)h * D;
         const float inv = 1.f / lrow;
 #pragma unroll
         for (int e = 0; e < D; ++e) orow[e] = acc[e] * inv;
-        p.lse[((int64_t)b * p.Hq + h) * N + i] = mrow + logf(lrow);
+        p.lse[sq.lse0 + (int64_t)h * sq.hs + i] = mrow + logf(lrow);
     }
 }
 
@@ -518,6 +526,8 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     p.k_rs = s.k_rs;
     p.v_rs = s.v_rs;
     p.o_rs = s.o_rs;
+    p.cu_seqlens = s.cu;
+    p.total = s.total;
     const int grp = s.Hq / s.Hkv;
     p.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
     p.pos_blocks = kWaves / p.heads_per_wg;
@@ -543,8 +553,9 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
 
 hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
                                float *lse, const AttnShape &s, hipStream_t stream) {
-    FwdF32Params p{q,      k,      v,      o,      lse,           s.N,  s.q_rs,   s.k_rs,
-                   s.v_rs, s.o_rs, (int32_t)s.B, s.Hq, s.Hkv, s.scale, s.causal, 0};
+    FwdF32Params p{q,      k,      v,    o,       lse,          s.N,  s.q_rs, s.k_rs,
+                   s.v_rs, s.o_rs, s.cu, s.total, (int32_t)s.B, s.Hq, s.Hkv,  s.scale,
+                   s.causal, 0};
     p.n_rblk = (int32_t)((s.N + kF32Rows - 1) / kF32Rows);
     const int64_t items = (int64_t)p.n_rblk * p.B * p.Hq;
     if (items <= 0) return hipSuccess;

@@ -34,6 +34,44 @@ struct FastDiv32 {
     }
 };
 
+// The tokens of sequence b of a call and where its statistics live.  With
+// no table (cu == nullptr) the call holds B sequences of N tokens each, lse
+// is [B][Hq][N] and the backward statistics are [B][Hq][2][N].  With a table
+// the call holds packed variable-length sequences: sequence b is tokens
+// [cu[b], cu[b+1]) of `total`, lse is [Hq][total] and the statistics are
+// [Hq][2][total].  Table entries are clamped into [0, total] and a length to
+// at most N (the caller's maximum), so a malformed table can give wrong
+// values but never an access outside the tensors.
+struct SeqRange {
+    int64_t tok0;  // first token of the sequence
+    int32_t len;   // its number of tokens
+    int64_t lse0;  // lse index of (head 0, row 0); head h adds h * hs
+    int64_t st0;   // statistics index of (head 0, row 0); head h adds 2h * hs, D is hs further
+    int64_t hs;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const int32_t *cu, int b, int64_t N, int32_t Hq,
+                                              int64_t total) {
+    SeqRange r;
+    if (cu) {
+        int64_t a = cu[b], e = cu[b + 1];
+        a = a < 0 ? 0 : (a > total ? total : a);
+        e = e < a ? a : (e > total ? total : e);
+        r.tok0 = a;
+        r.len = (int32_t)(e - a < N ? e - a : N);
+        r.lse0 = a;
+        r.st0 = a;
+        r.hs = total;
+    } else {
+        r.tok0 = (int64_t)b * N;
+        r.len = (int32_t)N;
+        r.lse0 = (int64_t)b * Hq * N;
+        r.st0 = 2 * r.lse0;
+        r.hs = N;
+    }
+    return r;
+}
+
 // Lets `kernel` take `bytes` of dynamic LDS (the default limit is 64 KB).
 template <typename KernelT>
 inline hipError_t allow_lds(KernelT kernel, size_t bytes) {
@@ -58,6 +96,11 @@ struct AttnShape {
     float scale;
     int32_t causal;
     int64_t q_rs, k_rs, v_rs, o_rs, do_rs, dq_rs, dk_rs, dv_rs;  // token strides, elements
+    // Packed variable-length sequences: B sequences given by the device table
+    // cu (B + 1 entries) over `total` tokens, N the longest; nullptr for B
+    // sequences of N tokens.
+    const int32_t *cu = nullptr;
+    int64_t total = 0;
 };
 
 hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,

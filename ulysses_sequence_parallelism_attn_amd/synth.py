@@ -179,3 +179,26 @@ def random_bits(shape, dtype: str, seed: int) -> np.ndarray:
     if dtype == "f32":
         return rng.integers(0, 1 << 32, size=n, dtype=np.uint32).reshape(shape)
     raise ValueError(dtype)
+
+
+def length_mix(total: int, seed: int, lo: int = 512, hi: int = 16384) -> np.ndarray:
+    """Document lengths of a packed variable-length batch of `total` tokens.
+
+    Lengths are drawn log-uniformly in [lo, hi] (many short documents, a few long
+    ones) until they cover `total`; the last one is cut to fit.  The pages give no
+    length distribution; this mix only exercises ragged, unaligned boundaries and
+    a wide spread of per-document work.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out, used = [], 0
+    while used < total:
+        n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        n = min(max(n, 1), total - used)
+        out.append(n)
+        used += n
+    return np.array(out, dtype=np.int64)
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """int32 token offsets [0, l0, l0 + l1, ...] of packed sequences."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
