@@ -51,8 +51,10 @@ def lib():
                                       ctypes.c_int, vp, vp, vp]
         for name in ("oracle_relayout_s2h", "oracle_relayout_h2s"):
             getattr(L, name).argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
+        for name in ("oracle_relayout_s2h_heads", "oracle_relayout_h2s_heads"):
+            getattr(L, name).argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, i64]
         for f in (L.oracle_attn_fwd_rows, L.oracle_attn_bwd, L.oracle_relayout_s2h,
-                  L.oracle_relayout_h2s):
+                  L.oracle_relayout_h2s, L.oracle_relayout_s2h_heads, L.oracle_relayout_h2s_heads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -83,6 +85,31 @@ def relayout_h2s(y: np.ndarray) -> np.ndarray:
     rc = lib().oracle_relayout_h2s(_ptr(y), _ptr(out), C, N, Hs * P, d, P, y.itemsize)
     if rc:
         raise RuntimeError(f"oracle_relayout_h2s failed ({rc})")
+    return out
+
+
+def relayout_s2h_heads(x: np.ndarray, P: int, h0: int, Hc: int) -> np.ndarray:
+    """[C, N, H, d] -> [C, P, N, Hc, d]: heads h0 .. h0+Hc-1 of every rank's slice."""
+    x = np.ascontiguousarray(x)
+    C, N, H, d = x.shape
+    out = np.empty((C, P, N, Hc, d), dtype=x.dtype)
+    rc = lib().oracle_relayout_s2h_heads(_ptr(x), _ptr(out), C, N, H, d, P, h0, Hc, x.itemsize)
+    if rc:
+        raise RuntimeError(f"oracle_relayout_s2h_heads failed ({rc})")
+    return out
+
+
+def relayout_h2s_heads(y: np.ndarray, out: np.ndarray, h0: int) -> np.ndarray:
+    """Writes y [C, P, N, Hc, d] into heads h0 .. h0+Hc-1 of every rank's slice of `out`
+    [C, N, H, d] (in place; the other heads are left as they are) and returns `out`."""
+    y = np.ascontiguousarray(y)
+    if not out.flags.c_contiguous or out.dtype != y.dtype:
+        raise ValueError("out must be a C-contiguous array of y's dtype")
+    C, P, N, Hc, d = y.shape
+    H = out.shape[2]
+    rc = lib().oracle_relayout_h2s_heads(_ptr(y), _ptr(out), C, N, H, d, P, h0, Hc, y.itemsize)
+    if rc:
+        raise RuntimeError(f"oracle_relayout_h2s_heads failed ({rc})")
     return out
 
 

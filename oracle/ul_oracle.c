@@ -399,3 +399,60 @@ int oracle_relayout_h2s(const uint8_t *in, uint8_t *out, int64_t C, int64_t N, i
                 }
     return 0;
 }
+
+/*
+ * The same exchange for a chunk of heads: Hc heads starting h0 heads into
+ * every rank's slice (a rank working through its heads a few at a time).
+ *   out[c][r][t][hh][e] = in[c][t][r*(H/P) + h0 + hh][e],   hh < Hc
+ * out is [C][P][N][Hc][d].
+ */
+int oracle_relayout_s2h_heads(const uint8_t *in, uint8_t *out, int64_t C, int64_t N, int64_t H,
+                              int64_t d, int64_t P, int64_t h0, int64_t Hc, int64_t elt)
+{
+    if (C < 1 || N < 1 || H < 1 || d < 1 || P < 1 || H % P != 0 || N % P != 0 || elt < 1)
+        return 1;
+    const int64_t Hs = H / P;
+    if (h0 < 0 || Hc < 1 || h0 + Hc > Hs)
+        return 2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t c = 0; c < C; ++c)
+        for (int64_t r = 0; r < P; ++r)
+            for (int64_t t = 0; t < N; ++t)
+                for (int64_t hh = 0; hh < Hc; ++hh)
+                    for (int64_t e = 0; e < d; ++e) {
+                        const int64_t h = r * Hs + h0 + hh;
+                        const int64_t src = ((c * N + t) * H + h) * d + e;
+                        const int64_t dst = (((c * P + r) * N + t) * Hc + hh) * d + e;
+                        memcpy(out + dst * elt, in + src * elt, (size_t)elt);
+                    }
+    return 0;
+}
+
+/*
+ * Its inverse on the chunk: writes heads r*(H/P) + h0 .. + Hc - 1 of every
+ * token of out [C][N][H][d] from in [C][P][N][Hc][d] and leaves the other
+ * heads of out as they are.  Loops over the destination heads it owns.
+ */
+int oracle_relayout_h2s_heads(const uint8_t *in, uint8_t *out, int64_t C, int64_t N, int64_t H,
+                              int64_t d, int64_t P, int64_t h0, int64_t Hc, int64_t elt)
+{
+    if (C < 1 || N < 1 || H < 1 || d < 1 || P < 1 || H % P != 0 || N % P != 0 || elt < 1)
+        return 1;
+    const int64_t Hs = H / P;
+    if (h0 < 0 || Hc < 1 || h0 + Hc > Hs)
+        return 2;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t c = 0; c < C; ++c)
+        for (int64_t t = 0; t < N; ++t)
+            for (int64_t h = 0; h < H; ++h) {
+                const int64_t r = h / Hs, hh = h % Hs - h0;
+                if (hh < 0 || hh >= Hc)
+                    continue;
+                for (int64_t e = 0; e < d; ++e) {
+                    const int64_t src = (((c * P + r) * N + t) * Hc + hh) * d + e;
+                    const int64_t dst = ((c * N + t) * H + h) * d + e;
+                    memcpy(out + dst * elt, in + src * elt, (size_t)elt);
+                }
+            }
+    return 0;
+}

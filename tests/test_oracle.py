@@ -375,6 +375,50 @@ def test_relayout_rejects_bad_shapes():
         ON.relayout_s2h(np.zeros((1, 6, 8, 2), np.uint16), 4)  # 6 tokens not divisible by 4
 
 
+@pytest.mark.parametrize("C,N,H,d,P,h0,Hc", [(3, 16, 8, 4, 2, 1, 2), (1, 12, 6, 3, 3, 0, 1),
+                                             (2, 8, 16, 8, 4, 2, 2), (3, 4, 4, 5, 1, 0, 4)])
+@pytest.mark.parametrize("dtype", [np.uint16, np.uint32])
+def test_head_chunk_relayout_matches_numpy_slice(C, N, H, d, P, h0, Hc, dtype):
+    """The head-chunk exchange is a slice of the heads inside every rank's slice, then the
+    same transpose (a library routine)."""
+    rng = np.random.Generator(np.random.PCG64(155))
+    x = rng.integers(0, np.iinfo(dtype).max, size=(C, N, H, d), dtype=dtype)
+    y = ON.relayout_s2h_heads(x, P, h0, Hc)
+    ref = x.reshape(C, N, P, H // P, d)[:, :, :, h0:h0 + Hc].transpose(0, 2, 1, 3, 4)
+    assert np.array_equal(y, ref)
+
+
+def test_head_chunks_compose_to_the_full_exchange():
+    """Chunks that partition each rank's slice, put side by side, are the full s2h; writing
+    them back with h2s_heads over a garbage-filled tensor rebuilds the input exactly, and a
+    single chunk's write leaves every other head untouched."""
+    C, N, H, d, P = 2, 12, 12, 3, 3
+    Hs = H // P
+    rng = np.random.Generator(np.random.PCG64(156))
+    x = rng.integers(0, 65535, size=(C, N, H, d), dtype=np.uint16)
+    chunks = [(0, 1), (1, 2), (3, 1)]  # (h0, Hc) covering 0 .. Hs-1
+    parts = [ON.relayout_s2h_heads(x, P, h0, Hc) for h0, Hc in chunks]
+    assert np.array_equal(np.concatenate(parts, axis=3), ON.relayout_s2h(x, P))
+    back = rng.integers(0, 65535, size=x.shape, dtype=np.uint16)
+    before = back.copy()
+    ON.relayout_h2s_heads(parts[1], back, 1)
+    owned = np.zeros(H, bool)
+    for r in range(P):
+        owned[r * Hs + 1: r * Hs + 3] = True
+    assert np.array_equal(back[:, :, ~owned], before[:, :, ~owned])
+    assert np.array_equal(back[:, :, owned], x[:, :, owned])
+    for (h0, Hc), y in zip(chunks, parts):
+        ON.relayout_h2s_heads(y, back, h0)
+    assert np.array_equal(back, x)
+
+
+def test_head_chunk_relayout_rejects_bad_ranges():
+    x = np.zeros((1, 8, 8, 2), dtype=np.uint16)
+    for h0, Hc in ((-1, 1), (0, 0), (3, 2), (4, 1)):  # rank slices hold 4 heads at P = 2
+        with pytest.raises(RuntimeError):
+            ON.relayout_s2h_heads(x, 2, h0, Hc)
+
+
 # ----------------------------------------------------------------------------- planted mistakes
 
 
