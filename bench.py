@@ -13,7 +13,9 @@ One step is one pass of the whole path over one batch of synthetic input:
 A second measurement, `fused_relayout`, times the same rank's forward and backward through
 the token-strided entry points on sequence-sharded world tensors, i.e. the step with both
 relayouts fused into the attention's own loads and stores.  A third, `varlen`, times forward
-and backward over the same 65536 tokens packed as variable-length sequences.
+and backward over the same 65536 tokens packed as variable-length sequences.  A fourth,
+`head_chunked`, runs the whole step one KV group at a time through head-chunk exchanges,
+so the exchange buffer holds one chunk of heads.
 
 The backward runs as its three C-ABI stages (D/lse preparation, the dQ pass, the dK/dV
 pass) with events between them, so each kernel's duration is measured on the stream it
@@ -189,6 +191,57 @@ def fused_step(B, torch, q, k, v, do, wl, P, args, ms_relayout_path) -> dict:
             "rank": r, "q_tok_stride": views["q"].stride(1), "kv_tok_stride": views["k"].stride(1)}
 
 
+def chunked_step(B, torch, q, k, v, do, wl, x, P, args, ms_whole) -> dict:
+    """The step with the rank's heads taken one KV group at a time: for each group, the
+    head-chunk exchange of the QKV stack into a buffer of that group's heads, forward and
+    backward on the group, and the reverse exchange of the chunk.  Same bytes and FLOPs as
+    the whole-slice step; the exchange buffer holds one chunk."""
+    C, N, H, d = x.shape
+    Hs = H // P
+    groups = wl.Hkv
+    hc = Hs // groups  # heads of the stack per chunk
+    grp = wl.Hq // wl.Hkv
+    ybuf = torch.empty((C, P, N, hc, d), dtype=x.dtype, device=x.device)
+    x2 = torch.empty_like(x)
+    parts = []
+    for gi in range(groups):
+        qs, ks = slice(gi * grp, (gi + 1) * grp), slice(gi, gi + 1)
+        t = {"q": q[:, :, qs].contiguous(), "k": k[:, :, ks].contiguous(),
+             "v": v[:, :, ks].contiguous(), "do": do[:, :, qs].contiguous()}
+        t["o"] = torch.empty_like(t["q"])
+        t["dq"], t["dk"], t["dv"] = (torch.empty_like(t[n]) for n in ("q", "k", "v"))
+        t["lse"] = torch.empty((wl.B, grp, wl.N), dtype=torch.float32, device=q.device)
+        t["ws"] = torch.empty(B.workspace_bytes(wl.B, wl.N, grp, 1, wl.d, B.UL_BF16),
+                              dtype=torch.uint8, device=q.device)
+        parts.append(t)
+
+    def step():
+        for gi, t in enumerate(parts):
+            B.relayout_s2h_heads(x, P, gi * hc, hc, out=ybuf)
+            B.attn_fwd(t["q"], t["k"], t["v"], wl.scale, True, out=t["o"], lse=t["lse"])
+            B.attn_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], wl.scale, True,
+                       workspace=t["ws"], dq=t["dq"], dk=t["dk"], dv=t["dv"])
+            B.relayout_h2s_heads(ybuf, x2, gi * hc)
+
+    for _ in range(args.warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    return {"ms_per_step": ms,
+            "tflops": (wl.flops_fwd() + wl.flops_bwd()) / (ms * 1e-3) / 1e12,
+            "chunks": groups, "heads_per_chunk": {"stack": hc, "q": grp, "kv": 1},
+            "exchange_buffer_bytes": ybuf.numel() * ybuf.element_size(),
+            "whole_slice_buffer_bytes": C * P * N * Hs * d * x.element_size(),
+            "time_vs_whole_slice": ms / ms_whole}
+
+
 VARLEN_SEED = 3008  # seed of the packed-sequence length mix
 
 
@@ -240,6 +293,8 @@ def main() -> int:
                     help="skip the strided (relayout-free) variant of the step")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length variant of the step")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the head-chunked variant of the step")
     ap.add_argument("--cpu-prefix", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
@@ -411,6 +466,9 @@ def main() -> int:
         out["fused_relayout"] = fused_step(B, torch, q, k, v, do, wl, P, args, ms_per_step)
     if not args.no_varlen:
         out["varlen"] = varlen_step(B, torch, synth, q, k, v, do, wl, args)
+    if not args.no_chunked:
+        del y, x2
+        out["head_chunked"] = chunked_step(B, torch, q, k, v, do, wl, x, P, args, ms_per_step)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(st, wl, min(args.cpu_prefix, wl.N))
     print(json.dumps(out), flush=True)

@@ -19,7 +19,8 @@
  *   ul_attn_*_strided the same on token-strided views, so that a rank's head
  *                     slice is read from and written to sequence-sharded
  *                     buffers in place (no relayout pass around attention);
- *   ul_attn_*_varlen  the same over packed variable-length sequences.
+ *   ul_attn_*_varlen  the same over packed variable-length sequences;
+ *   ul_relayout_*_heads  the exchange for a chunk of each rank's heads.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  No call
@@ -280,6 +281,36 @@ ul_status ul_relayout_s2h(const void *in, void *out, int64_t C, int64_t N, int32
  */
 ul_status ul_relayout_h2s(const void *in, void *out, int64_t C, int64_t N, int32_t H,
                           int32_t head_dim, int32_t P, int32_t dtype, void *stream);
+
+/*
+ * The exchange for a chunk of heads: heads h0 .. h0+Hc-1 of every rank's
+ * slice.  A rank that works through its heads a few at a time (to cap the
+ * activation and exchange-buffer memory of very long sequences: "Ulysses
+ * Unleashed: Context Parallelism with Fragmentation by Heads" describes
+ * splitting the attention work into fine-grained head fragments for that
+ * purpose) exchanges one chunk per call, so its head-sharded buffers hold Hc
+ * heads instead of H/P.
+ *
+ *   ul_relayout_s2h_heads:  in  [C][N][H][head_dim] (sequence-sharded world)
+ *                           out [C][P][N][Hc][head_dim]
+ *                           out[c][r][t][hh][e] = in[c][t][r*(H/P) + h0 + hh][e]
+ *   ul_relayout_h2s_heads:  in  [C][P][N][Hc][head_dim]
+ *                           out [C][N][H][head_dim]: writes exactly the chunk's
+ *                           heads r*(H/P) + h0 + hh of every token and leaves
+ *                           every other head of out untouched.
+ *
+ * Over a set of chunks that partition [0, H/P) these compose to
+ * ul_relayout_s2h / ul_relayout_h2s.  Bits are moved, never changed.
+ * Requirements and errors as ul_relayout_s2h, plus SHAPE when h0 < 0,
+ * Hc < 1 or h0 + Hc > H/P.  OVERLAP compares the [C][N][H][d] side with
+ * the [C][P][N][Hc][d] side.
+ */
+ul_status ul_relayout_s2h_heads(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                                int32_t head_dim, int32_t P, int32_t h0, int32_t Hc,
+                                int32_t dtype, void *stream);
+ul_status ul_relayout_h2s_heads(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                                int32_t head_dim, int32_t P, int32_t h0, int32_t Hc,
+                                int32_t dtype, void *stream);
 
 /* Static, NUL-terminated name of a status code ("UL_OK", ...). */
 const char *ul_status_str(ul_status s);

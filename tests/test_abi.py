@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_fwd_varlen",
                           "ul_attn_bwd", "ul_attn_bwd_stages", "ul_attn_bwd_strided",
                           "ul_attn_bwd_varlen", "ul_attn_bwd_workspace_bytes",
-                          "ul_relayout_s2h", "ul_relayout_h2s", "ul_status_str"}
+                          "ul_relayout_s2h", "ul_relayout_h2s", "ul_relayout_s2h_heads",
+                          "ul_relayout_h2s_heads", "ul_status_str"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -256,3 +257,20 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+@pytest.mark.parametrize("fn", ["ul_relayout_s2h_heads", "ul_relayout_h2s_heads"])
+@pytest.mark.parametrize("args,code", [
+    ((0, A + BIG, 3, 64, 32, 128, 4, 0, 4, 1), 1),
+    ((A, A + BIG, 0, 64, 32, 128, 4, 0, 4, 1), 2),
+    ((A, A + BIG, 3, 64, 30, 128, 4, 0, 4, 1), 3),   # H % P
+    ((A, A + BIG, 3, 66, 32, 128, 4, 0, 4, 1), 3),   # N % P
+    ((A, A + BIG, 3, 64, 32, 128, 4, -1, 4, 1), 2),  # h0 < 0
+    ((A, A + BIG, 3, 64, 32, 128, 4, 0, 0, 1), 2),   # empty chunk
+    ((A, A + BIG, 3, 64, 32, 128, 4, 5, 4, 1), 2),   # past the rank's 8 heads
+    ((A, A + BIG, 3, 64, 32, 128, 4, 0, 4, 9), 4),
+    ((A, A + 4096, 3, 64, 32, 128, 4, 0, 4, 1), 7),  # ranges overlap
+])
+def test_relayout_heads_validation(L, fn, args, code):
+    a = [ctypes.c_void_p(args[0]), ctypes.c_void_p(args[1]), *args[2:], None]
+    assert getattr(L, fn)(*a) == code

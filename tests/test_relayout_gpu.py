@@ -75,3 +75,113 @@ def test_relayout_is_deterministic_and_writes_everything():
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     assert torch.equal(B.relayout_h2s(y1).view(torch.int16), x.view(torch.int16))
+
+
+# ---------------------------------------------------------------- head chunks
+
+
+@pytest.mark.parametrize("C,N,H,d,P,h0,Hc,dtype", [
+    (3, 256, 8, 64, 2, 1, 2, "bf16"),
+    (2, 96, 12, 128, 3, 0, 4, "bf16"),     # the whole slice: the full exchange
+    (1, 60, 8, 3, 2, 3, 1, "bf16"),        # 6-byte segments: 2-byte units
+    (3, 64, 16, 128, 4, 2, 2, "f32"),
+    (1, 1000, 32, 128, 4, 4, 4, "bf16"),   # one KV group of an 8-head slice
+])
+def test_relayout_heads_match_oracle(C, N, H, d, P, h0, Hc, dtype):
+    from ulysses_sequence_parallelism_attn_amd import binding as B
+
+    print(f"[relayout-heads] C={C} N={N} H={H} d={d} P={P} h0={h0} Hc={Hc} {dtype}", flush=True)
+    x = synth.random_bits((C, N, H, d), dtype, 500 + N)
+    xd = _bits_to_device(x, dtype)
+    yd = B.relayout_s2h_heads(xd, P, h0, Hc)
+    torch.cuda.synchronize()
+    assert np.array_equal(_device_bits(yd, dtype), ON.relayout_s2h_heads(x, P, h0, Hc))
+    # the inverse writes exactly the chunk's heads of a pre-filled tensor
+    z = synth.random_bits((C, P, N, Hc, d), dtype, 501 + N)
+    base = synth.random_bits((C, N, H, d), dtype, 502 + N)
+    out = _bits_to_device(base.copy(), dtype)
+    B.relayout_h2s_heads(_bits_to_device(z, dtype), out, h0)
+    torch.cuda.synchronize()
+    expect = ON.relayout_h2s_heads(z, base.copy(), h0)
+    assert np.array_equal(_device_bits(out, dtype), expect)
+
+
+def test_relayout_heads_full_size_chunks_compose():
+    """[3, 65536, 32, 128] bf16 at P = 4 in two chunks of 4 heads: the chunks side by side are
+    the full exchange, and writing both back rebuilds the input, byte for byte."""
+    from ulysses_sequence_parallelism_attn_amd import binding as B
+
+    C, N, H, d, P = 3, 65536, 32, 128, 4
+    print("[relayout-heads] full-size chunk composition", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(510)
+    x = torch.randint(-32768, 32767, (C, N, H, d), dtype=torch.int16, device="cuda",
+                      generator=g).view(torch.bfloat16)
+    full = B.relayout_s2h(x, P)
+    back = torch.zeros_like(x)
+    for h0 in (0, 4):
+        part = B.relayout_s2h_heads(x, P, h0, 4)
+        assert torch.equal(part.view(torch.int16), full[:, :, :, h0:h0 + 4].view(torch.int16))
+        B.relayout_h2s_heads(part, back, h0)
+        del part
+    torch.cuda.synchronize()
+    assert torch.equal(back.view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_head_chunked_attention_matches_whole_slice(dtype):
+    """A rank's attention done one KV group at a time through chunked exchanges equals the
+    whole-slice path (exchange, attention over all of the rank's heads, reverse exchange),
+    bit for bit: heads are independent and each head gets the same per-block work."""
+    import math
+
+    from ulysses_sequence_parallelism_attn_amd import binding as B
+
+    N, P, Hq_r, Hkv_r = 512, 2, 4, 2          # per rank: 4 query heads, 2 KV heads
+    d = 128 if dtype == "bf16" else 64
+    grp = Hq_r // Hkv_r
+    scale = 1.0 / math.sqrt(d)
+    print(f"[relayout-heads] chunked attention {dtype}", flush=True)
+    qx = _bits_to_device(synth.encode(synth.normal_f32((2, N, P * Hq_r, d), 520), dtype), dtype)
+    kvx = _bits_to_device(synth.encode(synth.normal_f32((2, N, P * Hkv_r, d), 521), dtype), dtype)
+    # world tensors: [q, dO] stacked (C = 2) and [k, v] stacked (C = 2)
+
+    def whole():
+        yq, ykv = B.relayout_s2h(qx, P), B.relayout_s2h(kvx, P)
+        o = torch.empty_like(yq[:1])
+        grads_q = torch.empty_like(yq[:1])
+        grads_kv = torch.empty_like(ykv)
+        for r in range(P):
+            q, do = yq[0, r][None], yq[1, r][None]
+            k, v = ykv[0, r][None], ykv[1, r][None]
+            o_r, lse = B.attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), scale, True)
+            dq, dk, dv = B.attn_bwd(q.contiguous(), k.contiguous(), v.contiguous(), o_r,
+                                    do.contiguous(), lse, scale, True)
+            o[0, r], grads_q[0, r], grads_kv[0, r], grads_kv[1, r] = o_r[0], dq[0], dk[0], dv[0]
+        return B.relayout_h2s(o), B.relayout_h2s(grads_q), B.relayout_h2s(grads_kv)
+
+    def chunked():
+        o_w = torch.full((1, N, P * Hq_r, d), float("nan"), dtype=qx.dtype, device="cuda")
+        dq_w = torch.full_like(o_w, float("nan"))
+        dkv_w = torch.full_like(kvx, float("nan"))
+        for gi in range(Hkv_r):  # one KV group (grp query heads, 1 KV head) per chunk
+            yq = B.relayout_s2h_heads(qx, P, gi * grp, grp)
+            ykv = B.relayout_s2h_heads(kvx, P, gi, 1)
+            o_c = torch.empty_like(yq[:1])
+            dq_c = torch.empty_like(yq[:1])
+            dkv_c = torch.empty_like(ykv)
+            for r in range(P):
+                q, do = yq[0, r][None].contiguous(), yq[1, r][None].contiguous()
+                k, v = ykv[0, r][None].contiguous(), ykv[1, r][None].contiguous()
+                o_r, lse = B.attn_fwd(q, k, v, scale, True)
+                dq, dk, dv = B.attn_bwd(q, k, v, o_r, do, lse, scale, True)
+                o_c[0, r], dq_c[0, r], dkv_c[0, r], dkv_c[1, r] = o_r[0], dq[0], dk[0], dv[0]
+            B.relayout_h2s_heads(o_c, o_w, gi * grp)
+            B.relayout_h2s_heads(dq_c, dq_w, gi * grp)
+            B.relayout_h2s_heads(dkv_c, dkv_w, gi)
+        return o_w, dq_w, dkv_w
+
+    ref, got = whole(), chunked()
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+    for name, a, b in zip(("o", "dq", "dk|dv"), got, ref):
+        assert torch.equal(bits(a), bits(b)), name

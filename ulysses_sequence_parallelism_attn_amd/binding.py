@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp]
             f.restype = ctypes.c_int
+        for name in ("ul_relayout_s2h_heads", "ul_relayout_h2s_heads"):
+            f = getattr(L, name)
+            f.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, i32, i32, vp]
+            f.restype = ctypes.c_int
         L.ul_status_str.argtypes = [ctypes.c_int]
         L.ul_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -281,3 +285,32 @@ def relayout_h2s(y, out=None, stream=None):
                                _stream(stream))
     _check("ul_relayout_h2s", st)
     return x
+
+
+def relayout_s2h_heads(x, P: int, h0: int, Hc: int, out=None, stream=None):
+    """[C, N, H, d] -> [C, P, N, Hc, d]: heads h0 .. h0+Hc-1 of every rank's slice."""
+    import torch
+
+    _require(x, "x")
+    C, N, H, d = x.shape
+    if P < 1 or H % P:
+        raise ValueError("H must be a multiple of P")
+    y = torch.empty((C, P, N, Hc, d), dtype=x.dtype, device=x.device) if out is None else out
+    _require(y, "out")
+    st = lib().ul_relayout_s2h_heads(_ptr(x), _ptr(y), C, N, H, d, P, h0, Hc, _dtype_code(x),
+                                     _stream(stream))
+    _check("ul_relayout_s2h_heads", st)
+    return y
+
+
+def relayout_h2s_heads(y, out, h0: int, stream=None):
+    """Writes y [C, P, N, Hc, d] into heads h0 .. h0+Hc-1 of every rank's slice of `out`
+    [C, N, H, d]; the other heads of `out` are left as they are.  Returns `out`."""
+    _require(y, "y")
+    _require(out, "out")
+    C, P, N, Hc, d = y.shape
+    H = out.shape[2]
+    st = lib().ul_relayout_h2s_heads(_ptr(y), _ptr(out), C, N, H, d, P, h0, Hc, _dtype_code(y),
+                                     _stream(stream))
+    _check("ul_relayout_h2s_heads", st)
+    return out

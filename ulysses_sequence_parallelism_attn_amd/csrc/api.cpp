@@ -129,6 +129,25 @@ ul_status check_relayout(const void *in, const void *out, int64_t C, int64_t N, 
     return UL_OK;
 }
 
+// A head chunk of the exchange: the world side is [C][N][H][d], the chunk side
+// [C][P][N][Hc][d] with 0 <= h0 and h0 + Hc <= H/P.
+ul_status check_relayout_heads(const void *in, const void *out, int64_t C, int64_t N, int32_t H,
+                               int32_t head_dim, int32_t P, int32_t h0, int32_t Hc, int32_t dtype,
+                               bool to_head) {
+    if (!in || !out) return UL_ERR_NULL;
+    if (C < 1 || N < 1 || H < 1 || head_dim < 1) return UL_ERR_SHAPE;
+    if (P < 1 || H % P != 0 || N % P != 0) return UL_ERR_DIVISIBILITY;
+    if (h0 < 0 || Hc < 1 || (int64_t)h0 + Hc > H / P) return UL_ERR_SHAPE;
+    if (dtype != UL_F32 && dtype != UL_BF16) return UL_ERR_UNSUPPORTED;
+    int64_t world, chunk;
+    if (!elems(&world, {C, N, H, head_dim, elt_size(dtype)}) ||
+        !elems(&chunk, {C, P, N, Hc, head_dim, elt_size(dtype)}))
+        return UL_ERR_SHAPE;
+    const Range w = range(to_head ? in : out, world), c = range(to_head ? out : in, chunk);
+    if (overlap(w, c)) return UL_ERR_OVERLAP;
+    return UL_OK;
+}
+
 ul_status from_hip(hipError_t e) { return e == hipSuccess ? UL_OK : UL_ERR_HIP; }
 
 }  // namespace
@@ -303,6 +322,28 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
 }  // namespace
 
 extern "C" {
+
+ul_status ul_relayout_s2h_heads(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                                int32_t head_dim, int32_t P, int32_t h0, int32_t Hc, int32_t dtype,
+                                void *stream) {
+    const ul_status st =
+        check_relayout_heads(in, out, C, N, H, head_dim, P, h0, Hc, dtype, true);
+    if (st != UL_OK) return st;
+    return from_hip(ul::launch_relayout_heads(in, out, C, N, H, head_dim, P, h0, Hc,
+                                              elt_size(dtype), true,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+ul_status ul_relayout_h2s_heads(const void *in, void *out, int64_t C, int64_t N, int32_t H,
+                                int32_t head_dim, int32_t P, int32_t h0, int32_t Hc, int32_t dtype,
+                                void *stream) {
+    const ul_status st =
+        check_relayout_heads(in, out, C, N, H, head_dim, P, h0, Hc, dtype, false);
+    if (st != UL_OK) return st;
+    return from_hip(ul::launch_relayout_heads(in, out, C, N, H, head_dim, P, h0, Hc,
+                                              elt_size(dtype), false,
+                                              static_cast<hipStream_t>(stream)));
+}
 
 ul_status ul_attn_fwd_strided(const void *q, const void *k, const void *v, void *o, float *lse,
                               int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,

@@ -86,6 +86,10 @@ inline hipError_t allow_lds(KernelT kernel, size_t bytes) {
 
 hipError_t launch_relayout(const void *in, void *out, int64_t C, int64_t N, int64_t H, int64_t d,
                            int64_t P, int64_t elt, bool to_head, hipStream_t stream);
+// The exchange of heads h0 .. h0+Hc-1 of every rank's slice (h0 + Hc <= H/P).
+hipError_t launch_relayout_heads(const void *in, void *out, int64_t C, int64_t N, int64_t H,
+                                 int64_t d, int64_t P, int64_t h0, int64_t Hc, int64_t elt,
+                                 bool to_head, hipStream_t stream);
 
 // Sizes of one attention call.  Token t of batch b of a tensor starts
 // (b*N + t) * its token stride elements from the tensor's base pointer; head
