@@ -50,7 +50,7 @@ struct SeqRange {
     int64_t hs;
 };
 
-__device__ __forceinline__ SeqRange seq_range(const int32_t *cu, int b, int64_t N, int32_t Hq,
+__host__ __device__ __forceinline__ SeqRange seq_range(const int32_t *cu, int b, int64_t N, int32_t Hq,
                                               int64_t total) {
     SeqRange r;
     if (cu) {
