@@ -46,7 +46,7 @@ METRIC = "causal attn fwd+bwd TFLOP/s and % bf16 MFMA peak at N=64K, 8q/2kv head
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
-KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "relayout.hip", "mfma_tile.h"]
+KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "relayout.hip", "mfma_tile.h", "ul_internal.h"]
 
 
 def kernel_hash() -> str:
