@@ -146,6 +146,27 @@ def cpu_baseline(st: dict, wl, n_prefix: int) -> dict:
     }
 
 
+def copy_ceiling(torch, x, reps: int = 10) -> dict:
+    """A plain device-to-device copy of the relayout's bytes (torch's copy kernel): the
+    practical ceiling an HBM-bound permutation of that size can approach, for context."""
+    src = x.view(-1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    nbytes = 2.0 * src.numel() * src.element_size()
+    del dst
+    return {"ms": ms, "GB/s": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes,
+            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def fused_step(B, torch, q, k, v, do, wl, P, args, ms_relayout_path) -> dict:
     """The same rank's forward and backward with the relayouts fused away: the token-strided
     calls read the rank's head slice (rank P-1, the largest offsets) straight out of
@@ -462,6 +483,7 @@ def main() -> int:
         "roofline_all": roof,
         "kernel_hash": kernel_hash(),
     }
+    out["copy_ceiling"] = copy_ceiling(torch, x)
     if not args.no_fused:
         out["fused_relayout"] = fused_step(B, torch, q, k, v, do, wl, P, args, ms_per_step)
     if not args.no_varlen:
