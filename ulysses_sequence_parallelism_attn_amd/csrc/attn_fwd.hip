@@ -361,6 +361,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
         constexpr bool FULL = decltype(full)::value;
         const bool more = t + 2 < ntiles;
         UL_LDS unsigned char *nx = lds + stage(t + 2);
+        // The wave feeding the MFMA pipe takes issue priority over the other
+        // wave of its SIMD (busy with its softmax) until its half ends.
+        __builtin_amdgcn_s_setprio(2);
         if constexpr (FULL) {
             fwd_gemm<D, true, true, kDmaPerWave>(acc, pf, s, qf, ring, stage(t - 1), stage(t), fo,
                                                  [&](int k) {
@@ -374,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
             if (t < ntiles && visible(t)) fwd_gemm<D, false, true, 0>(acc, pf, s, qf, ring, 0, stage(t), fo, none);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         if (more)
             wait_vm_barrier<kDmaPerWave>();
         else
