@@ -1,0 +1,90 @@
+"""The dK/dV producer's early barrier, checked on the compiled gfx950 code (CPU only).
+
+Before the barrier that hands its P / dS fragments to the consumers, a dK/dV producer waits
+only until its own P / dS writes have retired, and leaves the next step's operand reads in
+flight (`s_waitcnt lgkmcnt(K)` rather than lgkmcnt(0)).  That is exact only while the
+compiled code keeps three facts, which this test checks in the assembly of every kernel that
+contains the producer (the dK/dV kernels and the merged backward kernel, head_dim 64 and
+128):
+* between the last LDS write before the wait and the wait there are exactly K LDS reads and
+  no other LDS or scalar-memory operation;
+* nothing touches LDS between the wait and the barrier;
+* no scalar memory operation is issued after the kernel's first barrier (lgkmcnt then counts
+  LDS operations only, which retire in order).  This one is checked on the standalone dK/dV
+  kernels: the merged kernel also holds the dQ body, whose scalar loads are on a branch that
+  no dK/dV workgroup takes, while its dK/dV body is the same inlined code.
+K is the count the source defines, kKvAhead + kStatReads, read from the source.
+"""
+
+import re
+import shutil
+import subprocess
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+CSRC = ROOT / "ulysses_sequence_parallelism_attn_amd" / "csrc"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not Path(hipcc).exists():
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "attn_bwd.s"
+    subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++20", "-Xclang", "-target-feature",
+                    "-Xclang", "-packed-fp32-ops", f"-I{ROOT / 'include'}", "--cuda-device-only", "-S",
+                    str(CSRC / "attn_bwd.hip"), "-o", str(out)], check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(text):
+    """Instruction lines of each dK/dV-containing kernel, by symbol."""
+    out = {}
+    for m in re.finditer(r"^(_Z\S*dkdv_bf16_kernel\S*):", text, re.M):
+        body = text[m.end():text.index("s_endpgm", m.end())]
+        out[m.group(1)] = [ln.strip() for ln in body.split("\n")
+                           if ln.strip() and not ln.strip().startswith((";", "."))]
+    return out
+
+
+LDS = re.compile(r"^ds_")
+SMEM = re.compile(r"^s_(load|buffer_load|store|buffer_store|atomic)")
+
+
+def _expected_count():
+    src = (CSRC / "attn_bwd.hip").read_text()
+    ahead = int(re.search(r"constexpr int kKvAhead = (\d+);", src).group(1))
+    stat = re.search(r"constexpr int kStatReads = ([\d *+-]+);", src).group(1)
+    return ahead + eval(stat, {"__builtins__": {}})
+
+
+def test_producer_waits_retire_exactly_the_pds_writes(asm):
+    kernels = _kernels(asm)
+    assert len(kernels) == 4, sorted(kernels)  # dkdv<64>, dkdv<128>, dq_dkdv<64>, dq_dkdv<128>
+    K = _expected_count()
+    assert 0 < K <= 15
+    for name, ins in kernels.items():
+        waits = [i for i, x in enumerate(ins) if x == f"s_waitcnt lgkmcnt({K})"]
+        checked = 0
+        for i in waits:
+            k = K
+            j = i
+            while j > 0 and not ins[j].startswith("ds_write"):
+                j -= 1
+            if not ins[j].startswith("ds_write"):
+                continue
+            between = ins[j + 1:i]
+            reads = [x for x in between if x.startswith("ds_read")]
+            others = [x for x in between if (LDS.match(x) and not x.startswith("ds_read")) or SMEM.match(x)]
+            assert len(reads) == k and not others, (name, i, k, len(reads), others)
+            n = i + 1
+            while not ins[n].startswith("s_barrier"):
+                assert not LDS.match(ins[n]) and not SMEM.match(ins[n]), (name, ins[n])
+                n += 1
+            checked += 1
+        assert checked >= 6, (name, checked)  # one per unrolled producer step
+        if "dq_dkdv" not in name:
+            first_barrier = next(i for i, x in enumerate(ins) if x.startswith("s_barrier"))
+            assert not any(SMEM.match(x) for x in ins[first_barrier:]), name

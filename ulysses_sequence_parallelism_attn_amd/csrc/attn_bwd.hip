@@ -534,6 +534,7 @@ struct DkvStats {
     f32x4 l[2][2], d[2][2];
 };
 
+constexpr int kStatReads = 2 * 2 * 2;  // LDS reads (one 16-byte read each) in dkdv_stats
 __device__ __forceinline__ void dkdv_stats(DkvStats &t, uint32_t stat) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
@@ -752,8 +753,18 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
                 advance(cmp);
                 dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
                 dkdv_stats(stats, stat + T::stat_stage(NX));
-                // P / dS stored (and the operands read) before the barrier
-                __builtin_amdgcn_s_waitcnt(0xc07f);
+                // P / dS stored before the barrier; the next step's operand
+                // reads may stay in flight across it (they are waited for
+                // at their first use).  LDS operations retire in order, the
+                // loop issues no scalar memory operation, and after the last
+                // P / dS write exactly kKvAhead fragment reads and
+                // kStatReads statistics reads follow (16-byte reads of
+                // distinct addresses, which the compiler cannot merge), so
+                // waiting until at most that many are outstanding retires
+                // exactly the writes.
+                constexpr int kReadsAfterPds = kKvAhead + kStatReads;
+                static_assert(kReadsAfterPds <= 15, "lgkmcnt immediate");
+                __builtin_amdgcn_s_waitcnt(0xc07f | (kReadsAfterPds << 8));
                 fence_barrier();
             });
         return;
