@@ -82,11 +82,13 @@ CALIBRATION_BYTES = float(1 << 30)
 
 
 def _pmc_per_kernel(csv_path: Path, counter: str) -> dict:
-    """Mean counter value per dispatch for each known kernel (and the calibration copy)."""
+    """Mean counter value per dispatch for each known kernel, and the value of the calibration
+    copy: the first copy dispatch of the run (later copies have other sizes)."""
     import csv
 
     acc: dict = {}
-    for r in csv.DictReader(open(csv_path)):
+    rows = sorted(csv.DictReader(open(csv_path)), key=lambda r: int(r["Dispatch_Id"]))
+    for r in rows:
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
@@ -94,7 +96,7 @@ def _pmc_per_kernel(csv_path: Path, counter: str) -> dict:
         for pat, short in KERNEL_NAMES:
             if pat in name:
                 key = short
-        if key is None:
+        if key is None or (key == CALIBRATION_KERNEL and key in acc):
             continue
         acc.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
@@ -316,6 +318,8 @@ def main() -> int:
                     help="skip the packed variable-length variant of the step")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the head-chunked variant of the step")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the device-copy reference for the relayout's bytes")
     ap.add_argument("--cpu-prefix", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
@@ -483,7 +487,8 @@ def main() -> int:
         "roofline_all": roof,
         "kernel_hash": kernel_hash(),
     }
-    out["copy_ceiling"] = copy_ceiling(torch, x)
+    if not args.no_copy_ceiling:
+        out["copy_ceiling"] = copy_ceiling(torch, x)
     if not args.no_fused:
         out["fused_relayout"] = fused_step(B, torch, q, k, v, do, wl, P, args, ms_per_step)
     if not args.no_varlen:
