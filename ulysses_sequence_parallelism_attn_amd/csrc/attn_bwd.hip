@@ -10,7 +10,9 @@
 //   dk_j = scale sum_{h in group, i} ds_ij q_i,  dv_j = sum_{h in group, i} p_ij dO_i.
 //
 // Three launches on the caller's stream, no atomics (bit-reproducible):
-//  1. pre:   D = rowsum(dO * O) and lse in log2 units -> workspace (fp32).
+//  1. pre:   -D = -rowsum(dO * O) and lse in log2 units -> workspace (fp32).
+//            D is stored negated so that dP - D can start as the dP
+//            MFMA's accumulator (see dkdv_sdp).
 //  2. dq:    per (b, KV head, query block), like the forward: streams K/V
 //            tiles, recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T and
 //            accumulates dQ^T += K^T dS^T in registers.
@@ -39,7 +41,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ============================================================================ pre kernel
 
 // Workspace layout: for each (b, h), N floats of lse2 (= lse log2 e) then N
-// floats of D, so both statistics of a query tile are one block apart.
+// floats of -D, so both statistics of a query tile are one block apart.
 struct PreParams {
     const void *o, *dout;
     const float *lse;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
         const int64_t i = bi % p.N, b = bi / p.N;
         const int64_t bh = b * p.Hq + h;
         p.stats[(2 * bh) * p.N + i] = p.lse[bh * p.N + i] * kLog2e;
-        p.stats[(2 * bh + 1) * p.N + i] = acc;
+        p.stats[(2 * bh + 1) * p.N + i] = -acc;
     }
 }
 
@@ -149,9 +151,11 @@ struct DqOffs {
 //   SDP steps  S^T = K Q^T and dP^T = V dO^T of this tile (tiles at
 //              `cstage`), alternating per k-step.
 // With DQ the first kQAhead<D> fragments are already in `ring` (dq_prefetch).
+// dP^T starts from `nd` (-D of the lane's query row in every register), so the
+// stream leaves dP^T - D in `dp`.
 // `side(k)`, k < NSIDE, runs between MFMAs spread over the stream.
 template <int D, bool DQ, bool SDP, int NSIDE, typename Side>
-__device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f32x16 &s, f32x16 &dp,
+__device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f32x16 &s, f32x16 &dp, const f32x16 &nd,
                                         const bf16x8 *qf, const bf16x8 *dof, bf16x8 (&ring)[kQAhead<D>],
                                         uint32_t pstage, uint32_t cstage, const DqOffs<D> &o, Side &&side) {
     constexpr int EB = D / 32, KK = D / 16;
@@ -168,7 +172,7 @@ __device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f
     };
     if constexpr (SDP) {
         s = zero16();
-        dp = zero16();
+        dp = nd;
     }
     if constexpr (!DQ) {
 #pragma unroll
@@ -207,10 +211,10 @@ __device__ __forceinline__ void dq_prefetch(bf16x8 (&ring)[kQAhead<D>], uint32_t
 }
 
 // dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2), as two bf16 B
-// fragments of 16 keys.  MASK zeroes P past the causal diagonal and the
-// ragged end.
+// fragments of 16 keys; `dpd` already holds dP^T - D (dq_gemm).  MASK zeroes
+// P past the causal diagonal and the ragged end.
 template <bool MASK>
-__device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f32x16 &dp, float lse2, float Drow,
+__device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f32x16 &dpd, float lse2,
                                       int kg, int j0, int row, int N, int causal, float c) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -223,7 +227,7 @@ __device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f
                 const int j = j0 + ckey(r, kg);
                 if (j >= N || (causal && j > row)) pv = 0.f;
             }
-            ds[q] = pv * (dp[r] - Drow);
+            ds[q] = pv * dpd[r];
         }
         dsf[hh] = pack8(ds);
     }
@@ -275,7 +279,10 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     }
     const int64_t so = sq.st0 + (int64_t)h * 2 * sq.hs + (ok ? row : 0);
     const float lse2 = ok ? p.stats[so] : 0.f;
-    const float Drow = ok ? p.stats[so + sq.hs] : 0.f;
+    const float nDrow = ok ? p.stats[so + sq.hs] : 0.f;  // -D
+    f32x16 nd;  // the dP^T accumulator's starting value
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nd[r] = nDrow;
     // Retire these loads: inside the loop vmcnt counts only the tile loads.
     __builtin_amdgcn_s_waitcnt(0x70);
 
@@ -362,7 +369,7 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         const bool more = t + T::kAhead < ntiles;
         UL_LDS unsigned char *nx = lds + stage(t + T::kAhead);
         if constexpr (FULL) {
-            dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, qf, dof, ring, stage(t - 1), stage(t), fo,
+            dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), stage(t), fo,
                                                 [&](int k) {
                                                     if (more) issue_k(t + T::kAhead, k, nx);
                                                 });
@@ -370,9 +377,9 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
             if (more) issue(t + T::kAhead, nx);
             auto none = [](int) {};
             if (t >= 1 && visible(t - 1))
-                dq_gemm<D, true, false, 0>(dqacc, dsf, s, dp, qf, dof, ring, stage(t - 1), 0, fo, none);
+                dq_gemm<D, true, false, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), 0, fo, none);
             if (t < ntiles && visible(t))
-                dq_gemm<D, false, true, 0>(dqacc, dsf, s, dp, qf, dof, ring, 0, stage(t), fo, none);
+                dq_gemm<D, false, true, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, 0, stage(t), fo, none);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (more)
@@ -382,9 +389,9 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         __builtin_amdgcn_sched_barrier(0);
         if (FULL || (t < ntiles && visible(t))) {
             if constexpr (FULL)
-                dq_ds<false>(dsf, s, dp, lse2, Drow, kg, t * kDqKT, row, N, p.causal, c);
+                dq_ds<false>(dsf, s, dp, lse2, kg, t * kDqKT, row, N, p.causal, c);
             else
-                dq_ds<true>(dsf, s, dp, lse2, Drow, kg, t * kDqKT, row, N, p.causal, c);
+                dq_ds<true>(dsf, s, dp, lse2, kg, t * kDqKT, row, N, p.causal, c);
             dq_prefetch<D>(ring, stage(t), fo);
         }
         fence_barrier();
@@ -508,13 +515,15 @@ __device__ __forceinline__ void dkdv_sdp_prefetch(bf16x8 (&ring)[kKvAhead], uint
 
 // `side(k)`, k < NSIDE, runs between MFMAs spread over the stream (the tile
 // loads).
+// dP starts from `nd` (-D of each C register's row), so the stream leaves
+// dP - D in `dp` and the softmax saves a subtraction per element.
 template <int D, int NSIDE, typename Side>
-__device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const bf16x8 *kf, const bf16x8 *vf,
-                                         bf16x8 (&ring)[kKvAhead], uint32_t qst, const uint32_t *oq,
-                                         const uint32_t *od, Side &&side) {
+__device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const f32x16 &nd, const bf16x8 *kf,
+                                         const bf16x8 *vf, bf16x8 (&ring)[kKvAhead], uint32_t qst,
+                                         const uint32_t *oq, const uint32_t *od, Side &&side) {
     constexpr int NSTEP = 2 * (D / 16), EVERY = NSTEP / NSIDE;
     s = zero16();
-    dp = zero16();
+    dp = nd;
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
         const bf16x8 a = ring[st % kKvAhead];
@@ -528,33 +537,41 @@ __device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const bf16x8 *kf
     }
 }
 
-// The statistics of this lane group's 16 rows (lse2 and D for the 8-row runs
-// hh, rows 0-3 then 4-7 of each), read from a stage's block at `stat`.
+// The statistics of this lane group's 16 rows (the 8-row runs hh, rows 0-3
+// then 4-7 of each), read from a stage's block at `stat`: lse2 by run, and
+// -D as one register block in C order (register hh*8 + x*4 + q), the dP
+// accumulator's starting value.
 struct DkvStats {
-    f32x4 l[2][2], d[2][2];
+    f32x4 l[2][2];
+    f32x16 nd;
 };
 
 constexpr int kStatReads = 2 * 2 * 2;  // LDS reads (one 16-byte read each) in dkdv_stats
 __device__ __forceinline__ void dkdv_stats(DkvStats &t, uint32_t stat) {
+    f32x4 d[2][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             t.l[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + hh * 64 + x * 16));
-            t.d[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + kQT * 4 + hh * 64 + x * 16));
+            d[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + kQT * 4 + hh * 64 + x * 16));
         }
+    const f32x8 d0 = __builtin_shufflevector(d[0][0], d[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x8 d1 = __builtin_shufflevector(d[1][0], d[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    t.nd = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 }
 
 // P = exp2(S c - lse2) (zero where MASK finds a key past the row or past N)
-// and dS = P (dP - D) as bf16 B fragments at this lane's slot `pds`.  C
-// register r of lane group kg holds query row ckey(r, kg): two runs of 8
-// consecutive rows (16*hh + 8*kg ..), whose statistics are in `t`.
+// and dS = P (dP - D) as bf16 B fragments at this lane's slot `pds`; `dpd`
+// already holds dP - D (dkdv_sdp).  C register r of lane group kg holds
+// query row ckey(r, kg): two runs of 8 consecutive rows (16*hh + 8*kg ..),
+// whose lse2 values are in `t`.
 template <bool MASK>
-__device__ __forceinline__ void dkdv_softmax(const f32x16 &s, const f32x16 &dp, const DkvStats &t, uint32_t pds,
+__device__ __forceinline__ void dkdv_softmax(const f32x16 &s, const f32x16 &dpd, const DkvStats &t, uint32_t pds,
                                              int kg, int r0, int key, int N, int causal, float c) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 l0 = t.l[hh][0], l1 = t.l[hh][1], d0 = t.d[hh][0], d1 = t.d[hh][1];
+        const f32x4 l0 = t.l[hh][0], l1 = t.l[hh][1];
         float pv[8], ds[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -564,7 +581,7 @@ __device__ __forceinline__ void dkdv_softmax(const f32x16 &s, const f32x16 &dp, 
                 const int i = r0 + ckey(r, kg);
                 pv[q] = (i >= N || key >= N || (causal && key > i)) ? 0.f : pv[q];
             }
-            ds[q] = pv[q] * (dp[r] - (q < 4 ? d0[q] : d1[q - 4]));
+            ds[q] = pv[q] * dpd[r];
         }
         *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + hh * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(pv));
         *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + (2 + hh) * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(ds));
@@ -738,7 +755,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         run(
             [&](int, auto stage) {  // MFMA half: S and dP of step i
                 constexpr int ST = decltype(stage)::value;
-                dkdv_sdp<D, 1>(s, dp, kf, vf, ring, T::q_stage(ST), oq, od, [](int) {});
+                dkdv_sdp<D, 1>(s, dp, stats.nd, kf, vf, ring, T::q_stage(ST), oq, od, [](int) {});
                 fence_barrier();
             },
             [&](int, auto stage) {  // P / dS of step i, then step i+1's operands
@@ -983,7 +1000,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
         acc[e] = 0.f;
     }
     const float lse = valid ? p.lse[sq.lse0 + (int64_t)h * sq.hs + ri] : 0.f;
-    const float Di = valid ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + ri] : 0.f;
+    const float nDi = valid ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + ri] : 0.f;  // -D
     const int64_t blk_last = (int64_t)rblk * kF32Rows + kF32Rows - 1;
     const int64_t kend = p.causal ? (blk_last + 1 < N ? blk_last + 1 : N) : N;
     for (int64_t j0 = 0; j0 < kend; j0 += kF32Keys) {
@@ -1006,7 +1023,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_bwd_dq_f32_kernel(BwdF32Params 
                 dp = fmaf(dov[e], vs[jj][e], dp);
             }
             const float pr = expf(s * p.scale - lse);
-            const float ds = pr * (dp - Di);
+            const float ds = pr * (dp + nDi);
 #pragma unroll
             for (int e = 0; e < D; ++e) acc[e] = fmaf(ds, ks[jj][e], acc[e]);
         }
@@ -1028,7 +1045,7 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
     __shared__ float ds_[kF32KvRows][D];
     __shared__ float kown[kF32KvKeys][D + 1];
     __shared__ float vown[kF32KvKeys][D + 1];
-    __shared__ float ls[kF32KvRows], Ds[kF32KvRows];
+    __shared__ float ls[kF32KvRows], nDs[kF32KvRows];  // lse, -D
     const int tid = threadIdx.x;
     const int bg = blockIdx.x % (p.B * p.Hkv);
     const int kblk = blockIdx.x / (p.B * p.Hkv);
@@ -1063,7 +1080,7 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
             if (tid < kF32KvRows) {
                 const int64_t i = i0 + tid;
                 ls[tid] = i < N ? p.lse[sq.lse0 + (int64_t)h * sq.hs + i] : 0.f;
-                Ds[tid] = i < N ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + i] : 0.f;
+                nDs[tid] = i < N ? p.stats[sq.st0 + (2 * (int64_t)h + 1) * sq.hs + i] : 0.f;
             }
             __syncthreads();
             for (int ii = 0; ii < kF32KvRows; ++ii) {
@@ -1075,7 +1092,7 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
                     dp = fmaf(ds_[ii][e], vown[tid][e], dp);
                 }
                 const float pr = expf(s * p.scale - ls[ii]);
-                const float dsv = pr * (dp - Ds[ii]);
+                const float dsv = pr * (dp + nDs[ii]);
 #pragma unroll
                 for (int e = 0; e < D; ++e) {
                     dk[e] = fmaf(dsv, qs[ii][e], dk[e]);
