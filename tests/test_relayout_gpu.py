@@ -185,3 +185,69 @@ def test_head_chunked_attention_matches_whole_slice(dtype):
     bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
     for name, a, b in zip(("o", "dq", "dk|dv"), got, ref):
         assert torch.equal(bits(a), bits(b)), name
+
+
+def test_relayout_above_2_32_units():
+    """The exchanges past 2^32 16-byte units (64-bit index path): [1, 2^23, 32, 128] bf16, P = 4,
+    64 GiB per side.  Each 16-byte unit of the input holds its own index (and a second word
+    derived from it), so every output unit is checked against the index the exchange's
+    definition names for it, out[c][r][t][hh][:] = in[c][t][r*Hs + hh][:], without a second
+    copy of the input.  The head-chunk exchanges (h0 = 4, Hc = 4) run at the same size."""
+    from ulysses_sequence_parallelism_attn_amd import binding as B
+
+    C, N, H, d, P = 1, 1 << 23, 32, 128, 4
+    Hs, upd = H // P, d * 2 // 16          # heads per rank; 16-byte units per head row
+    total = C * N * H * upd                # units per side
+    assert total >= 1 << 32
+    free, _ = torch.cuda.mem_get_info()
+    if free < 2 * total * 16 + (24 << 30):
+        pytest.skip("needs about 150 GB of free device memory")
+    K = 0x5DEECE66D
+    chunk = 1 << 27
+    x = torch.empty((C, N, H, d), dtype=torch.bfloat16, device="cuda")
+    x64 = x.view(-1).view(torch.int64).view(-1, 2)
+
+    def fill_pattern():
+        for a in range(0, total, chunk):
+            idx = torch.arange(a, min(a + chunk, total), dtype=torch.int64, device="cuda")
+            x64[a:a + len(idx), 0] = idx
+            x64[a:a + len(idx), 1] = idx ^ K
+
+    def check_pattern(t64, n_units, src_of):
+        for a in range(0, n_units, chunk):
+            h = torch.arange(a, min(a + chunk, n_units), dtype=torch.int64, device="cuda")
+            u = src_of(h)
+            assert torch.equal(t64[a:a + len(h), 0], u), f"units {a}..: wrong source"
+            assert torch.equal(t64[a:a + len(h), 1], u ^ K), f"units {a}..: second word"
+
+    def head_to_seq(h, hc, h0):
+        # head side [C][P][N][hc][upd] unit -> sequence side [C][N][H][upd] unit
+        eu, rest = h % upd, h // upd
+        hh, rest = rest % hc, rest // hc
+        t, rest = rest % N, rest // N
+        r, c = rest % P, rest // P
+        return ((c * N + t) * H + r * Hs + h0 + hh) * upd + eu
+
+    fill_pattern()
+    y = torch.empty((C, P, N, Hs, d), dtype=torch.bfloat16, device="cuda")
+    y64 = y.view(-1).view(torch.int64).view(-1, 2)
+    B.relayout_s2h(x, P, out=y)
+    torch.cuda.synchronize()
+    check_pattern(y64, total, lambda h: head_to_seq(h, Hs, 0))
+    x.zero_()
+    B.relayout_h2s(y, out=x)
+    torch.cuda.synchronize()
+    check_pattern(x64, total, lambda u: u)
+
+    h0, Hc = 4, 4
+    yc = y.view(-1)[:C * P * N * Hc * d].view(C, P, N, Hc, d)
+    B.relayout_s2h_heads(x, P, h0, Hc, out=yc)
+    torch.cuda.synchronize()
+    check_pattern(yc.view(-1).view(torch.int64).view(-1, 2), C * P * N * Hc * upd,
+                  lambda h: head_to_seq(h, Hc, h0))
+    x.view(C, N, P, Hs, d)[:, :, :, h0:h0 + Hc].zero_()
+    B.relayout_h2s_heads(yc, x, h0)
+    torch.cuda.synchronize()
+    check_pattern(x64, total, lambda u: u)
+    del x, y, yc, x64, y64
+    torch.cuda.empty_cache()
