@@ -52,29 +52,40 @@ struct PreParams {
     int32_t is_bf16;
 };
 
-// 16 lanes per (b, i, h) row; each lane reduces d/16 elements.
+// L lanes per (b, i, h) row, each with one 16-byte load of o and one of dout
+// (8 bf16 or 4 fp32 elements): L = 16 / 8 for bf16 at d = 128 / 64, 32 / 16
+// for fp32.  Rows are whole 16-byte granules (the head dim and every token
+// stride are multiples of 16 bytes), so the loads are aligned.
+template <bool BF16, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
+    constexpr int EPL = BF16 ? 8 : 4;
+    constexpr int L = D / EPL;
+    constexpr int RPB = 256 / L;  // rows per workgroup
     const int64_t rows = (int64_t)p.B * p.N * p.Hq;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int sub = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * RPB + (threadIdx.x / L);
+    const int sub = threadIdx.x % L;
     float acc = 0.f;
     if (row < rows) {
-        const int per = p.d / 16;
         // row = (b*N + i)*Hq + h
-        const int64_t tok = row / p.Hq, col = (row % p.Hq) * p.d + sub * per;
+        const int64_t tok = row / p.Hq, col = (row % p.Hq) * D + sub * EPL;
         const int64_t ob = tok * p.o_rs + col, gb = tok * p.do_rs + col;
-        if (p.is_bf16) {
-            const uint16_t *o = static_cast<const uint16_t *>(p.o) + ob;
-            const uint16_t *g = static_cast<const uint16_t *>(p.dout) + gb;
-            for (int e = 0; e < per; ++e) acc = fmaf(bf16_to_f32(g[e]), bf16_to_f32(o[e]), acc);
+        if constexpr (BF16) {
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.o) + ob);
+            const u32x4 g = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.dout) + gb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc = fmaf(bf16_to_f32((uint16_t)g[e]), bf16_to_f32((uint16_t)o[e]), acc);
+                acc = fmaf(bf16_to_f32((uint16_t)(g[e] >> 16)), bf16_to_f32((uint16_t)(o[e] >> 16)), acc);
+            }
         } else {
-            const float *o = static_cast<const float *>(p.o) + ob;
-            const float *g = static_cast<const float *>(p.dout) + gb;
-            for (int e = 0; e < per; ++e) acc = fmaf(g[e], o[e], acc);
+            const f32x4 o = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.o) + ob);
+            const f32x4 g = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.dout) + gb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(g[e], o[e], acc);
         }
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    for (int off = L / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, L);
     if (row < rows && sub == 0) {
         // row = (b*N + i)*Hq + h  ->  [b][h][i]
         const int64_t h = row % p.Hq;
@@ -1128,9 +1139,19 @@ static hipError_t launch_pre(const void *o, const void *dout, const float *lse, 
     const int64_t Bp = s.cu ? 1 : s.B, Np = s.cu ? s.total : s.N;
     PreParams pp{o, dout, lse, stats, Np, s.o_rs, s.do_rs, (int32_t)Bp, s.Hq, s.d, bf16 ? 1 : 0};
     const int64_t rows = Bp * Np * s.Hq;
-    const int64_t blocks = (rows + 15) / 16;
+    const int lanes = s.d / (bf16 ? 8 : 4);  // lanes per row, as the kernel takes them
+    const int64_t per_block = 256 / lanes;
+    const int64_t blocks = (rows + per_block - 1) / per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_pre_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, pp);
+    const dim3 grid((uint32_t)blocks), block(256);
+    if (bf16 && s.d == 128)
+        hipLaunchKernelGGL((bwd_pre_kernel<true, 128>), grid, block, 0, stream, pp);
+    else if (bf16)
+        hipLaunchKernelGGL((bwd_pre_kernel<true, 64>), grid, block, 0, stream, pp);
+    else if (s.d == 128)
+        hipLaunchKernelGGL((bwd_pre_kernel<false, 128>), grid, block, 0, stream, pp);
+    else
+        hipLaunchKernelGGL((bwd_pre_kernel<false, 64>), grid, block, 0, stream, pp);
     return hipGetLastError();
 }
 
