@@ -760,7 +760,15 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         bf16x8 ring[kKvAhead];
         f32x16 s, dp;
         DkvStats stats;
-        Cur cmp = first;
+        // The producer needs only each step's first row: r0 drops by a tile
+        // every grp steps.  Masked steps are those with r0 below mlo (the
+        // causal diagonal) or above mhi (the ragged end), and every step when
+        // the key block runs past N.  Past the last step r0 keeps dropping;
+        // that iteration's P / dS are masked and never used, and the
+        // producer addresses no memory with r0.
+        const int mlo = kb0 + kKeysPerWg > N ? INT_MAX : (p.causal ? kb0 + kKeysPerWg : INT_MIN);
+        const int mhi = N - kQT;
+        int r0 = first.r0, hc = grp;
         dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
         dkdv_stats(stats, stat + T::stat_stage(0));
         run(
@@ -771,14 +779,14 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             },
             [&](int, auto stage) {  // P / dS of step i, then step i+1's operands
                 constexpr int ST = decltype(stage)::value, NX = (ST + 1) % T::kStages;
-                const int r0 = cmp.r0;
-                const bool masked = (p.causal && r0 < kb0 + kKeysPerWg) || r0 + kQT > N ||
-                                    kb0 + kKeysPerWg > N;
-                if (masked)
+                if (r0 < mlo || r0 > mhi)
                     dkdv_softmax<true>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
                 else
                     dkdv_softmax<false>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
-                advance(cmp);
+                if (--hc == 0) {
+                    hc = grp;
+                    r0 -= kQT;
+                }
                 dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
                 dkdv_stats(stats, stat + T::stat_stage(NX));
                 // P / dS stored before the barrier; the next step's operand
@@ -852,11 +860,16 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // barrier ending the first half of step i (which follows the loads of
     // step i+kAhead-2) step i+1 must have landed: all but the newest kAhead-3
     // steps' worth.
+    // The operand reads of the first half need not retire before its
+    // barrier: their registers are waited for at the MFMAs that use them,
+    // and the memory they read is rewritten two barriers later at the
+    // earliest (P/dS buffer i % 2 by the producers' half of step i+1, the
+    // Q/dO stage by the loads issued in the second half of step i+1).
     auto wait_next = [&]() {
         if (stats_wave)
-            wait_vm<(T::kAhead - 3) * (kDmaPerWave + 2)>();
+            wait_vm_only<(T::kAhead - 3) * (kDmaPerWave + 2)>();
         else
-            wait_vm<(T::kAhead - 3) * kDmaPerWave>();
+            wait_vm_only<(T::kAhead - 3) * kDmaPerWave>();
     };
     Cur iss = first;
     [&]<int... J>(std::integer_sequence<int, J...>) {

@@ -333,6 +333,14 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
 }
 
+// The same wait on vector-memory operations only; LDS operations stay in
+// flight (their results are waited for at their first use).
+template <int N>
+__device__ __forceinline__ void wait_vm_only() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
     wait_vm<N>();
