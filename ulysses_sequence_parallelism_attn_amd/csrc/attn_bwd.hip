@@ -509,12 +509,16 @@ struct DkvTile {
 
 // ---- producer
 
-// S and dP of one step as a stream of 2 KK MFMAs, per k-step S then dP (A = Q
-// / dO row fragments of the tile at stage offset `qst`); the first kKvAhead
-// fragments are already in `ring` (read at the end of the previous step).
+// S and dP of one step as a stream of 2 KK MFMAs, the KK of S first, then
+// those of dP (A = Q / dO row fragments of the tile at stage offset `qst`), so
+// that S is complete well before the softmax needs it (measured: 1.4-2 %
+// faster than alternating them, 3.5 % faster than dP first); the first
+// kKvAhead fragments are already in `ring` (read at the end of the previous
+// step).
 template <int D>
 __device__ __forceinline__ bf16x8 dkdv_sdp_frag(int st, uint32_t qst, const uint32_t *oq, const uint32_t *od) {
-    return lds_frag_at((st % 2 == 0 ? oq[st / 2] : od[st / 2]) + qst);
+    constexpr int KK = D / 16;
+    return lds_frag_at((st < KK ? oq[st] : od[st - KK]) + qst);
 }
 
 template <int D>
@@ -539,10 +543,11 @@ __device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const f32x16 &nd
     for (int st = 0; st < NSTEP; ++st) {
         const bf16x8 a = ring[st % kKvAhead];
         if (st + kKvAhead < NSTEP) ring[st % kKvAhead] = dkdv_sdp_frag<D>(st + kKvAhead, qst, oq, od);
-        if (st % 2 == 0)
-            s = mfma32x32x16(a, kf[st / 2], s);
+        constexpr int KK = D / 16;
+        if (st < KK)
+            s = mfma32x32x16(a, kf[st], s);
         else
-            dp = mfma32x32x16(a, vf[st / 2], dp);
+            dp = mfma32x32x16(a, vf[st - KK], dp);
         if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
         __builtin_amdgcn_sched_barrier(0);
     }
