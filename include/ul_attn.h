@@ -195,8 +195,8 @@ ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o
 /*
  * The three stages of ul_attn_bwd, for callers that schedule them themselves.
  *
- *   UL_BWD_PREP   D_i = dout_i . o_i and lse in base-2 units, written to the
- *                 workspace (reads o, dout, lse);
+ *   UL_BWD_PREP   -D_i = -(dout_i . o_i) and lse in base-2 units, written to
+ *                 the workspace (reads o, dout, lse);
  *   UL_BWD_DQ     dq from q, k, v, dout and the workspace;
  *   UL_BWD_DKDV   dk and dv from q, k, v, dout and the workspace.
  *
