@@ -8,7 +8,7 @@ contains the producer (the dK/dV kernels and the merged backward kernel, head_di
 128):
 * between the last LDS write before the wait and the wait there are exactly K LDS reads and
   no other LDS or scalar-memory operation;
-* nothing touches LDS between the wait and the barrier;
+* the wait is the instruction right before the barrier (so nothing touches LDS in between);
 * no scalar memory operation is issued after the kernel's first barrier (lgkmcnt then counts
   LDS operations only, which retire in order).  This one is checked on the standalone dK/dV
   kernels: the merged kernel also holds the dQ body, whose scalar loads are on a branch that
@@ -66,7 +66,10 @@ def test_producer_waits_retire_exactly_the_pds_writes(asm):
     K = _expected_count()
     assert 0 < K <= 15
     for name, ins in kernels.items():
-        waits = [i for i, x in enumerate(ins) if x == f"s_waitcnt lgkmcnt({K})"]
+        # the producer's hand-over waits: lgkmcnt(K) right before a barrier (a
+        # compiler-placed wait with the same count elsewhere guards a register use)
+        waits = [i for i, x in enumerate(ins)
+                 if x == f"s_waitcnt lgkmcnt({K})" and ins[i + 1].startswith("s_barrier")]
         checked = 0
         for i in waits:
             k = K
