@@ -64,7 +64,7 @@ def test_producer_waits_retire_exactly_the_pds_writes(asm):
     kernels = _kernels(asm)
     assert len(kernels) == 4, sorted(kernels)  # dkdv<64>, dkdv<128>, dq_dkdv<64>, dq_dkdv<128>
     K = _expected_count()
-    assert 0 < K <= 15
+    assert 0 < K < 15  # lgkmcnt(15) encodes "no wait"
     for name, ins in kernels.items():
         # the producer's hand-over waits: lgkmcnt(K) right before a barrier (a
         # compiler-placed wait with the same count elsewhere guards a register use)

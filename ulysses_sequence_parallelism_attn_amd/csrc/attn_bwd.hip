@@ -804,7 +804,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
                 // waiting until at most that many are outstanding retires
                 // exactly the writes.
                 constexpr int kReadsAfterPds = kKvAhead + kStatReads;
-                static_assert(kReadsAfterPds <= 15, "lgkmcnt immediate");
+                static_assert(kReadsAfterPds < 15, "lgkmcnt immediate (15 encodes no wait)");
                 __builtin_amdgcn_s_waitcnt(0xc07f | (kReadsAfterPds << 8));
                 fence_barrier();
             });

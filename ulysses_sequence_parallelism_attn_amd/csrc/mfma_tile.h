@@ -329,7 +329,7 @@ __device__ __forceinline__ void fence_barrier() {
 // lgkmcnt[11:8] = 0).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    static_assert(N >= 0 && N < 63, "vmcnt immediate (63 encodes no wait)");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
 }
 
@@ -337,7 +337,7 @@ __device__ __forceinline__ void wait_vm() {
 // flight (their results are waited for at their first use).
 template <int N>
 __device__ __forceinline__ void wait_vm_only() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    static_assert(N >= 0 && N < 63, "vmcnt immediate (63 encodes no wait)");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
 }
 
