@@ -3,12 +3,12 @@
 
 One step is one pass of the whole path over one batch of synthetic input:
 
-  1. ul_relayout_s2h of a [3, 65536, 32, 128] bf16 QKV stack at P = 4
-     (the sequence -> head exchange, as a single-GPU permutation);
+  1. ul_relayout_s2h of the layer's [3, N, 32, 128] bf16 QKV stack at P = 4 (P = 8 for the
+     4q/1kv rank) (the sequence -> head exchange, as a single-GPU permutation);
   2. ul_attn_fwd: causal attention for one SP=4 rank of a Llama-3.1-8B-shaped layer
      (N = 65536, 8 query heads, 2 KV heads, head_dim 128, bf16);
   3. ul_attn_bwd: its dQ, dK, dV;
-  4. ul_relayout_h2s of the [3, 4, 65536, 8, 128] head-sharded stack (the reverse exchange).
+  4. ul_relayout_h2s of the [3, P, N, 32/P, 128] head-sharded stack (the reverse exchange).
 
 A second measurement, `fused_relayout`, times the same rank's forward and backward through
 the token-strided entry points on sequence-sharded world tensors, i.e. the step with both
@@ -123,29 +123,81 @@ def ingest_pmc(fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
-def cpu_baseline(st: dict, wl, n_prefix: int) -> dict:
-    """Time the float64 oracle on a causal prefix of the workload's own inputs."""
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(st: dict, wl, n_prefix: int, relayout_shape=None) -> dict:
+    """Time the float64 oracle on a causal prefix of the workload's own inputs; also the
+    oracle's full forward+backward of the N = 8192 rank workload and its scalar index-loop
+    relayout over the workload's exchange tensor, as reported context."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import attention as OA
+    from oracle import native as ON
+    from ulysses_sequence_parallelism_attn_amd import synth
 
     w = {n: OA.widen(a[:, :n_prefix], wl.dtype) for n, a in st.items()}
     t0 = time.perf_counter()
     OA.attn_bwd(w["q"], w["k"], w["v"], w["dout"], wl.scale, True)  # forward + backward
     dt = time.perf_counter() - t0
+    del w
     flops = 7.0 * n_prefix ** 2 * wl.Hq * wl.d
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {
+    out = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": len(os.sched_getaffinity(0)),
+        "blas_threads": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"float64 oracle forward+backward on the causal prefix N={n_prefix} of the "
                    f"N={wl.N} inputs (all {wl.Hq} query / {wl.Hkv} KV heads, d={wl.d}); "
                    f"{dt:.1f} s wall, rate in counted FLOPs (7*N^2*Hq*d)"),
         "seconds": dt,
     }
+    # the full N = 8192 rank workload, forward + backward
+    w2 = synth.WORKLOADS[2]
+    s2 = synth.attn_inputs(w2)
+    ww = {n: OA.widen(a, w2.dtype) for n, a in s2.items()}
+    del s2
+    t0 = time.perf_counter()
+    OA.attn_bwd(ww["q"], ww["k"], ww["v"], ww["dout"], w2.scale, True)
+    t2 = time.perf_counter() - t0
+    del ww
+    out["full_n8192"] = {"workload": w2.name, "seconds": t2,
+                         "tflops": (w2.flops_fwd() + w2.flops_bwd()) / t2 / 1e12}
+    # the scalar C relayout (one element per iteration, OpenMP over the outer loops)
+    if relayout_shape is not None:
+        C, N, H, d, P = relayout_shape
+        x = np.random.Generator(np.random.PCG64(7)).integers(0, 1 << 16, size=(C, N, H, d),
+                                                             dtype=np.uint16)
+        t0 = time.perf_counter()
+        ON.relayout_s2h(x, P)
+        tr = time.perf_counter() - t0
+        nbytes = 2.0 * x.nbytes
+        out["relayout_s2h_scalar"] = {"shape": [C, N, H, d], "P": P, "seconds": tr,
+                                      "GB/s": nbytes / tr / 1e9,
+                                      "omp_threads": int(os.environ.get("OMP_NUM_THREADS", "0"))
+                                      or len(os.sched_getaffinity(0))}
+    return out
 
 
 def copy_ceiling(torch, x, reps: int = 10) -> dict:
@@ -349,7 +401,7 @@ def main() -> int:
     from ulysses_sequence_parallelism_attn_amd import synth
 
     wl = synth.WORKLOADS[args.workload]
-    rl = synth.WORKLOADS[3].relayout  # (C, N, H, d, P)
+    rl = wl.exchange  # (C, N, H, d, P) of this workload's own QKV-stack exchange
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -358,7 +410,7 @@ def main() -> int:
     q, k, v, do = (up(st[n]) for n in ("q", "k", "v", "dout"))
     C, Nr, Hr, dr, P = rl
     gen = torch.Generator(device=dev)
-    gen.manual_seed(synth.seed_of(3, synth.SLOT_RELAYOUT))
+    gen.manual_seed(synth.seed_of(wl.wid, synth.SLOT_RELAYOUT))
     x = torch.randint(-32768, 32767, (C, Nr, Hr, dr), dtype=torch.int16, device=dev,
                       generator=gen).view(torch.bfloat16)
     y = torch.empty((C, P, Nr, Hr // P, dr), dtype=torch.bfloat16, device=dev)
@@ -437,9 +489,14 @@ def main() -> int:
     rows = wl.B * wl.N * wl.Hq
     prep_bytes = 2.0 * rows * wl.d * 2 + rows * 4 + 2 * rows * 4  # o, dout read; lse read; lse2, D written
 
-    def mfma(flop, n):
-        return {"bound": "mfma", "achieved": flop / (avg[n] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "algorithmic": flop}
+    def mfma(flop, n, performed=None):
+        r = {"bound": "mfma", "achieved": flop / (avg[n] * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+             "unit": "TFLOP/s", "algorithmic": flop}
+        if performed is not None:
+            r["performed"] = performed
+            r["achieved_performed"] = performed / (avg[n] * 1e-3) / 1e12
+            r["frac_performed"] = r["achieved_performed"] / PEAK_BF16_TFLOPS
+        return r
 
     def hbm(nbytes, n):
         return {"bound": "hbm", "achieved": nbytes / (avg[n] * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
@@ -449,7 +506,9 @@ def main() -> int:
         "relayout_s2h": hbm(rl_bytes, "relayout_s2h"),
         "attn_fwd": mfma(f_fwd, "attn_fwd"),
         "attn_bwd_prep": hbm(prep_bytes, "attn_bwd_prep"),
-        "attn_bwd_dq": mfma(6.0 * wl.d * pairs_x_heads, "attn_bwd_dq"),
+        # the method counts the dQ pass only for its dQ contraction (2d per pair; S and dP
+        # are counted once, in dK/dV); it performs S, dP and dQ (6d per pair)
+        "attn_bwd_dq": mfma(2.0 * wl.d * pairs_x_heads, "attn_bwd_dq", 6.0 * wl.d * pairs_x_heads),
         "attn_bwd_dkdv": mfma(8.0 * wl.d * pairs_x_heads, "attn_bwd_dkdv"),
         "relayout_h2s": hbm(rl_bytes, "relayout_h2s"),
     }
@@ -478,7 +537,7 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) Q/K/V/dO; random-bit relayout stack)",
         "config": {"workload": wl.name, "B": wl.B, "seq_len": wl.N, "q_heads": wl.Hq,
                    "kv_heads": wl.Hkv, "head_dim": wl.d, "causal": True,
-                   "relayout": {"shape": [C, Nr, Hr, dr], "P": P}, "parallelism": "sp4-rank-share"},
+                   "relayout": {"shape": [C, Nr, Hr, dr], "P": P}, "parallelism": f"sp{P}-rank-share"},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "attn_fwd_bwd_ms": attn_ms,
         "attn_fwd_bwd_tflops": flops_step / (attn_ms * 1e-3) / 1e12,
@@ -497,7 +556,10 @@ def main() -> int:
         del y, x2
         out["head_chunked"] = chunked_step(B, torch, q, k, v, do, wl, x, P, args, ms_per_step)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(st, wl, min(args.cpu_prefix, wl.N))
+        del x
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(st, wl, min(args.cpu_prefix, wl.N),
+                                           synth.WORKLOADS[3].exchange)
     print(json.dumps(out), flush=True)
     return 0
 

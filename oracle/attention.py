@@ -45,9 +45,15 @@ __all__ = [
     "probabilities",
 ]
 
-# Rows of the score matrix materialised at once (bounds memory only; every row
-# is computed independently by the same definition).
+# Rows of the score matrix materialised at once: at most 1024, and at most
+# about 2^26 scores per block for long key ranges (bounds memory only; every
+# row is computed independently by the same definition).
 _ROW_CHUNK = 1024
+_BLOCK_ELEMS = 1 << 26
+
+
+def _chunk(n_keys: int) -> int:
+    return max(1, min(_ROW_CHUNK, _BLOCK_ELEMS // max(1, n_keys)))
 
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -104,8 +110,9 @@ def _fwd_rows_one_head(qh, kg, vg, rows, scale, causal):
     """
     o = np.empty((len(rows), qh.shape[1]))
     lse = np.empty(len(rows))
-    for c0 in range(0, len(rows), _ROW_CHUNK):
-        r = rows[c0 : c0 + _ROW_CHUNK]
+    step = _chunk(kg.shape[0])
+    for c0 in range(0, len(rows), step):
+        r = rows[c0 : c0 + step]
         n = _key_end(r, kg.shape[0], causal)
         s = scale * (qh[r] @ kg[:n].T)
         s = np.where(_visible(r, n, causal), s, -np.inf)
@@ -196,8 +203,9 @@ def dq_rows(q, k, v, dout, scale: float, causal: bool = True, rows=None):
     for b in range(B):
         for h in range(Hq):
             g = _group(h, Hq, Hkv)
-            for c0 in range(0, len(rows), _ROW_CHUNK):
-                sl = slice(c0, c0 + _ROW_CHUNK)
+            step = _chunk(N)
+            for c0 in range(0, len(rows), step):
+                sl = slice(c0, c0 + step)
                 r = rows[sl]
                 n = _key_end(r, N, causal)
                 _, _, ds = _p_dp_ds(
@@ -227,8 +235,9 @@ def dkdv_rows(q, k, v, dout, scale: float, causal: bool = True, keys=None):
         for h in range(Hq):
             g = _group(h, Hq, Hkv)
             kg, vg = k[b, keys, g], v[b, keys, g]
-            for c0 in range(0, len(qrows), _ROW_CHUNK):
-                sl = slice(c0, c0 + _ROW_CHUNK)
+            step = _chunk(len(keys))
+            for c0 in range(0, len(qrows), step):
+                sl = slice(c0, c0 + step)
                 r = qrows[sl]
                 s = scale * (q[b, r, h] @ kg.T)
                 vis = (keys[None, :] <= r[:, None]) if causal else np.ones(s.shape, bool)
@@ -257,8 +266,9 @@ def attn_bwd(q, k, v, dout, scale: float, causal: bool = True):
     for b in range(B):
         for h in range(Hq):
             g = _group(h, Hq, Hkv)
-            for c0 in range(0, N, _ROW_CHUNK):
-                sl = slice(c0, c0 + _ROW_CHUNK)
+            step = _chunk(N)
+            for c0 in range(0, N, step):
+                sl = slice(c0, c0 + step)
                 r = rows[sl]
                 n = _key_end(r, N, causal)
                 p, _, ds = _p_dp_ds(

@@ -49,11 +49,18 @@ def lib():
                                            ctypes.c_int, vp, i64, vp, vp]
         L.oracle_attn_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
                                       ctypes.c_int, vp, vp, vp]
+        L.oracle_dq_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
+                                     ctypes.c_int, vp, i64, vp]
+        L.oracle_dkdv_rows.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
+                                       ctypes.c_int, vp, i64, vp, vp, vp, vp]
+        L.oracle_row_stats.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp,
+                                       ctypes.c_int, vp, vp]
         for name in ("oracle_relayout_s2h", "oracle_relayout_h2s"):
             getattr(L, name).argtypes = [vp, vp, i64, i64, i64, i64, i64, i64]
         for name in ("oracle_relayout_s2h_heads", "oracle_relayout_h2s_heads"):
             getattr(L, name).argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, i64]
-        for f in (L.oracle_attn_fwd_rows, L.oracle_attn_bwd, L.oracle_relayout_s2h,
+        for f in (L.oracle_attn_fwd_rows, L.oracle_attn_bwd, L.oracle_dq_rows, L.oracle_dkdv_rows,
+                  L.oracle_row_stats, L.oracle_relayout_s2h,
                   L.oracle_relayout_h2s, L.oracle_relayout_s2h_heads, L.oracle_relayout_h2s_heads):
             f.restype = ctypes.c_int
         _lib = L
@@ -145,3 +152,68 @@ def brute_bwd(q, k, v, dout, dtype: str, scale: float, causal: bool = True):
     if rc:
         raise RuntimeError(f"oracle_attn_bwd failed ({rc})")
     return dq, dk, dv
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, 0, None
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    return r, len(r), _ptr(r)
+
+
+def brute_fwd_rows(q, k, v, dtype: str, scale: float, causal: bool, rows):
+    """Scalar forward for the query rows `rows`: (o [B,R,Hq,d], lse [B,Hq,R]) in float64."""
+    q, k, v = (_stored(a, dtype) for a in (q, k, v))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    r, R, rp = _rows_arg(rows)
+    o = np.empty((B, R, Hq, d))
+    lse = np.empty((B, Hq, R))
+    rc = lib().oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _DT[dtype], B, N, Hq, Hkv, d,
+                                    scale, int(causal), rp, R, _ptr(o), _ptr(lse))
+    if rc:
+        raise RuntimeError(f"oracle_attn_fwd_rows failed ({rc})")
+    return o, lse
+
+
+def brute_dq_rows(q, k, v, dout, dtype: str, scale: float, causal: bool, rows):
+    """Scalar dQ for the query rows `rows`, [B,R,Hq,d] in float64."""
+    q, k, v, dout = (_stored(a, dtype) for a in (q, k, v, dout))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    r, R, rp = _rows_arg(rows)
+    dq = np.empty((B, R, Hq, d))
+    rc = lib().oracle_dq_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DT[dtype], B, N, Hq, Hkv, d,
+                              scale, int(causal), rp, R, _ptr(dq))
+    if rc:
+        raise RuntimeError(f"oracle_dq_rows failed ({rc})")
+    return dq
+
+
+def brute_dkdv_rows(q, k, v, dout, dtype: str, scale: float, causal: bool, keys,
+                    precomputed_stats: bool = False):
+    """Scalar dK, dV for the key rows `keys`, [B,R,Hkv,d] each in float64.
+
+    With precomputed_stats the row statistics (lse, D) of every query row come from the
+    scalar row-statistics loop first; otherwise they are recomputed per query row."""
+    q, k, v, dout = (_stored(a, dtype) for a in (q, k, v, dout))
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    r, R, rp = _rows_arg(keys)
+    dk = np.empty((B, R, Hkv, d))
+    dv = np.empty((B, R, Hkv, d))
+    lse = D = None
+    if precomputed_stats:
+        lse = np.empty((B, Hq, N))
+        D = np.empty((B, Hq, N))
+        rc = lib().oracle_row_stats(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DT[dtype], B, N, Hq,
+                                    Hkv, d, scale, int(causal), _ptr(lse), _ptr(D))
+        if rc:
+            raise RuntimeError(f"oracle_row_stats failed ({rc})")
+    rc = lib().oracle_dkdv_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _DT[dtype], B, N, Hq, Hkv,
+                                d, scale, int(causal), rp, R,
+                                None if lse is None else _ptr(lse),
+                                None if D is None else _ptr(D), _ptr(dk), _ptr(dv))
+    if rc:
+        raise RuntimeError(f"oracle_dkdv_rows failed ({rc})")
+    return dk, dv

@@ -4,13 +4,18 @@
   N = 8192 bf16 rank, and a sweep of ragged / GQA / head-dim / non-causal / batched shapes
   that span several tiles and a ragged tail.
 * At N = 65536, 98304 and 1048576 (the launch configuration the benchmark times): 512
-  seeded rows per head plus fixed edge rows for O, lse and dQ; the last 64 keys for dK and
-  dV (their causal sums are short); and exact gradient identities on the full tensors.
+  seeded rows per head plus fixed edge rows for O, lse and dQ; dK and dV at 512 seeded keys
+  per KV head drawn over the whole sequence plus keys 0, 1, 127, 128 and N/2 (over the last
+  16384 positions at N = 1048576), against values the oracle stored for exactly these inputs
+  (tests/golden/make_dkdv_samples.py; a key near the start needs the statistics of every
+  query row, minutes of fp64 CPU work); the last 64 keys against the oracle run here; and
+  exact gradient identities on the full tensors.
 * Determinism, full coverage of the outputs (NaN poison), causality and the Ulysses
   composition (per-rank attention on the relayout equals attention over all heads).
 """
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -130,6 +135,29 @@ def _invariants(gpu, wl):
     return out
 
 
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _check_stored_dkdv(gpu, wl):
+    """dK and dV of the GPU at the keys the oracle's stored file holds, per KV head."""
+    path = os.path.join(GOLDEN, f"dkdv_samples_w{wl.wid}.npz")
+    with np.load(path, allow_pickle=False) as z:
+        for g in range(wl.Hkv):
+            keys = z[f"keys_g{g}"]
+            dk_ref, dv_ref = z[f"dk_g{g}"].astype(np.float64), z[f"dv_g{g}"].astype(np.float64)
+            dk = H.to_f64(gpu["dk"][0, keys, g])
+            dv = H.to_f64(gpu["dv"][0, keys, g])
+            rk = H.check_rel_l2(dk, dk_ref, H.TOL_BF16_GRAD_RL2, f"{wl.name} dK sampled keys g{g}")
+            rv = H.check_rel_l2(dv, dv_ref, H.TOL_BF16_GRAD_RL2, f"{wl.name} dV sampled keys g{g}")
+            # the first keys carry the longest sums: report them on their own as well
+            first = keys < 256
+            if first.any():
+                H.check_rel_l2(dk[first], dk_ref[first], H.TOL_BF16_GRAD_RL2, f"{wl.name} dK first keys g{g}")
+                H.check_rel_l2(dv[first], dv_ref[first], H.TOL_BF16_GRAD_RL2, f"{wl.name} dV first keys g{g}")
+            print(f"[parity] {wl.name} g{g}: {len(keys)} keys [{keys.min()}, {keys.max()}] "
+                  f"dK rel-L2 {rk:.3g} dV rel-L2 {rv:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("wid", [3, 4, 5])
 def test_large_workload_sampled_parity(wid):
     wl = synth.WORKLOADS[wid]
@@ -155,6 +183,8 @@ def test_large_workload_sampled_parity(wid):
         dq_ref = OA.dq_rows(qh, kg, vg, doh, wl.scale, wl.causal, rows)
         dq_gpu = H.to_f64(gpu["dq"][:, rows, h:h + 1])
         H.check_rel_l2(dq_gpu, dq_ref, H.TOL_BF16_GRAD_RL2, f"{wl.name} dQ head {h}")
+    # dK / dV at the stored sampled keys of every KV head (whole range; last 16K at 1M)
+    _check_stored_dkdv(gpu, wl)
     # the last 64 keys of every KV head: their causal sums cover only the last rows
     keys = np.arange(wl.N - 64, wl.N)
     dk_ref, dv_ref = OA.dkdv_rows(w["q"], w["k"], w["v"], w["dout"], wl.scale, wl.causal, keys)

@@ -104,6 +104,50 @@ def test_probability_rows_sum_to_one(causal):
     np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
 
 
+def _torch_probabilities(q, k, scale, causal):
+    """Softmax of the scaled, masked scores by torch's CPU softmax (a library routine), with
+    each KV head repeated for its query heads."""
+    tq = torch.tensor(q).permute(0, 2, 1, 3)  # [B, Hq, N, d]
+    tk = torch.tensor(k).permute(0, 2, 1, 3)
+    tk = tk.repeat_interleave(q.shape[2] // k.shape[2], dim=1)
+    s = scale * (tq @ tk.transpose(-1, -2))
+    if causal:
+        N = q.shape[1]
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    return torch.softmax(s, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 23, 2, 2, 8), True), ((2, 31, 4, 1, 16), True),
+                                          ((1, 17, 6, 2, 8), False)])
+def test_probabilities_match_torch_softmax(shape, causal):
+    """P from the oracle equals torch's softmax of the scaled scores (GQA via repeated KV
+    heads), and P V equals the oracle's forward output."""
+    B, N, Hq, Hkv, d = shape
+    q, k, v, _ = _qkv(B, N, Hq, Hkv, d, 51)
+    P = OA.probabilities(q, k, 0.37, causal)
+    np.testing.assert_allclose(P, _torch_probabilities(q, k, 0.37, causal), rtol=0, atol=1e-14)
+    o, _ = OA.attn_fwd(q, k, v, 0.37, causal)
+    vr = np.repeat(v, Hq // Hkv, axis=2).transpose(0, 2, 1, 3)  # [B, Hq, N, d]
+    np.testing.assert_allclose((P @ vr).transpose(0, 2, 1, 3), o, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("mistake", ["scale", "group", "mask"])
+def test_probabilities_planted_mistakes_are_caught(monkeypatch, mistake):
+    """A wrong scale, group map or mask in the oracle's P fails the torch comparison."""
+    q, k, _, _ = _qkv(1, 23, 4, 2, 8, 52)
+    ref = _torch_probabilities(q, k, 0.5, True)
+    if mistake == "scale":
+        P = OA.probabilities(q, k, 0.5 * 1.01, True)
+    else:
+        if mistake == "group":
+            monkeypatch.setattr(OA, "_group", lambda h, Hq, Hkv: h % Hkv)
+        else:
+            monkeypatch.setattr(OA, "_visible",
+                                lambda rows, N, causal: np.arange(N)[None, :] < rows[:, None])
+        P = OA.probabilities(q, k, 0.5, True)
+    assert not (np.abs(P - ref) <= 1e-3).all()  # an all-masked row gives NaN: also a miss
+
+
 def test_lse_bounds():
     """max_j s_ij <= lse_i <= max_j s_ij + ln(i+1)."""
     B, N, Hq, Hkv, d = 1, 64, 2, 1, 16
@@ -327,6 +371,73 @@ def test_scalar_brute_force_agrees(dtype, causal):
     np.testing.assert_allclose(dq2, dq, atol=1e-12)
     np.testing.assert_allclose(dk2, dk, atol=1e-12)
     np.testing.assert_allclose(dv2, dv, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_scalar_row_subsets_agree(dtype, causal):
+    """The scalar C row-subset loops (forward rows, dQ rows, dK/dV key rows with the row
+    statistics recomputed per row or precomputed) agree with the matrix row functions the
+    long-sequence parity checks use, on unsorted subsets that include the first and the last
+    positions."""
+    B, N, Hq, Hkv, d = 2, 70, 4, 2, 16
+    st = synth.custom_inputs(B, N, Hq, Hkv, d, dtype, seed=9)
+    w = {n: OA.widen(a, dtype) for n, a in st.items()}
+    rows = np.array([69, 0, 33, 1, 64, 63])
+    o, lse = OA.attn_fwd(w["q"], w["k"], w["v"], 0.3, causal, rows)
+    o2, lse2 = ON.brute_fwd_rows(st["q"], st["k"], st["v"], dtype, 0.3, causal, rows)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, atol=1e-13)
+    dq = OA.dq_rows(w["q"], w["k"], w["v"], w["dout"], 0.3, causal, rows)
+    dq2 = ON.brute_dq_rows(st["q"], st["k"], st["v"], st["dout"], dtype, 0.3, causal, rows)
+    np.testing.assert_allclose(dq2, dq, atol=1e-12)
+    keys = np.array([0, 69, 12, 40])
+    dk, dv = OA.dkdv_rows(w["q"], w["k"], w["v"], w["dout"], 0.3, causal, keys)
+    for pre in (False, True):
+        dk2, dv2 = ON.brute_dkdv_rows(st["q"], st["k"], st["v"], st["dout"], dtype, 0.3, causal,
+                                      keys, precomputed_stats=pre)
+        np.testing.assert_allclose(dk2, dk, atol=1e-12)
+        np.testing.assert_allclose(dv2, dv, atol=1e-12)
+
+
+def test_row_chunking_does_not_change_results(monkeypatch):
+    """Blocking the rows differently (the memory bound of the matrix oracle) gives the same
+    values: every row is computed on its own."""
+    B, N, Hq, Hkv, d = 1, 90, 2, 1, 8
+    q, k, v, do = _qkv(B, N, Hq, Hkv, d, 141)
+    ref = OA.attn_bwd(q, k, v, do, 0.3, True)
+    keys = np.array([0, 45, 89])
+    ref_kv = OA.dkdv_rows(q, k, v, do, 0.3, True, keys)
+    monkeypatch.setattr(OA, "_BLOCK_ELEMS", 7 * N)  # 7-row blocks
+    got = OA.attn_bwd(q, k, v, do, 0.3, True)
+    for a, b in zip(got, ref):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    for a, b in zip(OA.dkdv_rows(q, k, v, do, 0.3, True, keys), ref_kv):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def test_sampled_keys_cover_the_range():
+    """The seeded key sample holds 512 distinct keys plus the fixed ones, inside the window."""
+    wl = synth.WORKLOADS[3]
+    keys = synth.sample_keys(wl, 0)
+    assert len(keys) >= 512 and np.all(np.diff(keys) > 0)
+    assert {0, 1, 127, 128, wl.N // 2, wl.N - 1} <= set(keys.tolist())
+    assert keys.min() == 0 and keys.max() == wl.N - 1
+    assert not np.array_equal(keys, synth.sample_keys(wl, 1))
+    w5 = synth.WORKLOADS[5]
+    k5 = synth.sample_keys(w5, 0, window=16384)
+    assert k5.min() == w5.N - 16384 and k5.max() == w5.N - 1 and len(k5) >= 512
+
+
+def test_stored_dkdv_samples_match_the_seeded_key_draw():
+    """The stored file's keys are the seeded draw of synth.sample_keys (so its values belong
+    to these inputs' sampled keys), and every workload above has a file."""
+    for wid, window in ((3, None), (4, None), (5, 16384)):
+        wl = synth.WORKLOADS[wid]
+        with np.load(os.path.join(GOLDEN, f"dkdv_samples_w{wid}.npz"), allow_pickle=False) as z:
+            for g in range(wl.Hkv):
+                assert np.array_equal(z[f"keys_g{g}"], synth.sample_keys(wl, g, window=window))
+                assert z[f"dk_g{g}"].shape == (len(z[f"keys_g{g}"]), wl.d)
 
 
 def test_widen_is_exact():

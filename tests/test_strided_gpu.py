@@ -12,8 +12,9 @@ whatever the strides, so every check here is bit-identical:
 * at the metric shape (N = 65536, world 32 query / 8 KV heads, P = 4) the last rank's
   strided call equals the dense call on contiguous copies of its slices.
 
-The dense path these are compared with is itself pinned to the float64 oracle by
-test_attn_gpu.py.
+Each rank's strided results are also compared element by element with the float64 oracle
+on that rank's head slice (ragged N, GQA, causal and full, bf16 and fp32, separate world
+tensors and a packed QKV tensor), at the path's tolerances.
 """
 
 import math
@@ -21,6 +22,7 @@ import math
 import numpy as np
 import pytest
 
+from oracle import attention as OA
 from ulysses_sequence_parallelism_attn_amd import synth
 
 from . import helpers as H
@@ -165,3 +167,94 @@ def test_fused_relayout_metric_shape_last_rank():
     _same(dKw[:, :, ks], dk_d, "dk")
     _same(dVw[:, :, ks], dv_d, "dv")
     assert torch.isnan(Ow[:, :, : r * Hq]).all() and torch.isnan(dKw[:, :, : r * Hkv]).all()
+
+
+# ---------------------------------------------------------------------------- against the oracle
+
+
+def _world_host(shape, dtype, seed):
+    """Stored world tensor (bf16 bits or float32) from seeded normals."""
+    return synth.encode(synth.normal_f32(shape, seed), dtype)
+
+
+def _check_rank(got: dict, st: dict, dtype, scale, causal, label):
+    """Compare one rank's strided results with the float64 oracle on its head slice."""
+    w = {n: OA.widen(a, dtype) for n, a in st.items()}
+    dq, dk, dv, o, lse = OA.attn_bwd(w["q"], w["k"], w["v"], w["dout"], scale, causal)
+    ref = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    g = {n: H.to_f64(t) for n, t in got.items()}
+    for n, x in g.items():
+        assert np.isfinite(x).all(), f"{label}: {n} has non-finite values"
+    if dtype == "f32":
+        for n in ("o", "lse", "dq", "dk", "dv"):
+            H.check_max_abs(g[n], ref[n], H.TOL_F32, f"{label} {n}")
+    else:
+        H.check_o_bf16(g["o"], ref["o"], f"{label} O")
+        H.check_max_abs(g["lse"], ref["lse"], H.TOL_BF16_LSE, f"{label} lse")
+        for n in ("dq", "dk", "dv"):
+            H.check_rel_l2(g[n], ref[n], H.TOL_BF16_GRAD_RL2, f"{label} {n}")
+
+
+@pytest.mark.parametrize("dtype,N,Hq,Hkv,d,P,causal", [
+    ("bf16", 700, 4, 2, 128, 2, True),
+    ("bf16", 332, 8, 2, 64, 4, True),
+    ("bf16", 300, 4, 1, 128, 2, False),
+    ("f32", 200, 2, 1, 64, 2, True),
+    ("f32", 150, 4, 2, 128, 2, False),
+])
+def test_strided_matches_oracle(dtype, N, Hq, Hkv, d, P, causal):
+    """Every rank reads its head slice from world tensors [1, N, P*H, d] at the world token
+    stride and writes O, dQ, dK, dV into world buffers; each slice is compared with the
+    oracle on that slice."""
+    B = _B()
+    label = f"strided-vs-oracle {dtype} N={N} {Hq}q{Hkv}kv d={d} P={P} {'causal' if causal else 'full'}"
+    print(f"[strided] {label}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    host = {"q": _world_host((1, N, P * Hq, d), dtype, 931), "k": _world_host((1, N, P * Hkv, d), dtype, 932),
+            "v": _world_host((1, N, P * Hkv, d), dtype, 933),
+            "dout": _world_host((1, N, P * Hq, d), dtype, 934)}
+    Qw, Kw, Vw, dOw = (H.to_device(host[n], dtype) for n in ("q", "k", "v", "dout"))
+    Ow, dQw = torch.full_like(Qw, float("nan")), torch.full_like(Qw, float("nan"))
+    dKw, dVw = torch.full_like(Kw, float("nan")), torch.full_like(Vw, float("nan"))
+    for r in range(P):
+        qs, ks = slice(r * Hq, (r + 1) * Hq), slice(r * Hkv, (r + 1) * Hkv)
+        q, k, v, do = Qw[:, :, qs], Kw[:, :, ks], Vw[:, :, ks], dOw[:, :, qs]
+        assert q.stride(1) == P * Hq * d and not q.is_contiguous()
+        _, lse = B.attn_fwd(q, k, v, scale, causal, out=Ow[:, :, qs])
+        B.attn_bwd(q, k, v, Ow[:, :, qs], do, lse, scale, causal, dq=dQw[:, :, qs],
+                   dk=dKw[:, :, ks], dv=dVw[:, :, ks])
+        torch.cuda.synchronize()
+        st = {"q": host["q"][:, :, qs], "k": host["k"][:, :, ks], "v": host["v"][:, :, ks],
+              "dout": host["dout"][:, :, qs]}
+        got = {"o": Ow[:, :, qs], "lse": lse, "dq": dQw[:, :, qs], "dk": dKw[:, :, ks],
+               "dv": dVw[:, :, ks]}
+        _check_rank(got, st, dtype, scale, causal, f"{label} rank {r}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_strided_packed_qkv_matches_oracle(dtype):
+    """Q, K, V as head slices of one packed [1, N, P*(Hq + 2 Hkv), d] tensor, gradients into
+    one packed buffer: each rank's results against the oracle."""
+    B = _B()
+    N, Hq, Hkv, P = 389, 4, 2, 2
+    d = 128 if dtype == "bf16" else 64
+    print(f"[strided] packed qkv vs oracle {dtype} N={N}", flush=True)
+    scale = 1.0 / math.sqrt(d)
+    Hw, Kw_ = P * Hq, P * Hkv
+    Xh = _world_host((1, N, Hw + 2 * Kw_, d), dtype, 941)
+    dOh = _world_host((1, N, Hw, d), dtype, 944)
+    X, dOw = H.to_device(Xh, dtype), H.to_device(dOh, dtype)
+    Ow = torch.full_like(dOw, float("nan"))
+    dX = torch.full_like(X, float("nan"))
+    for r in range(P):
+        qs = slice(r * Hq, (r + 1) * Hq)
+        ks = slice(Hw + r * Hkv, Hw + (r + 1) * Hkv)
+        vs = slice(Hw + Kw_ + r * Hkv, Hw + Kw_ + (r + 1) * Hkv)
+        q, k, v = X[:, :, qs], X[:, :, ks], X[:, :, vs]
+        _, lse = B.attn_fwd(q, k, v, scale, True, out=Ow[:, :, qs])
+        B.attn_bwd(q, k, v, Ow[:, :, qs], dOw[:, :, qs], lse, scale, True, dq=dX[:, :, qs],
+                   dk=dX[:, :, ks], dv=dX[:, :, vs])
+        torch.cuda.synchronize()
+        st = {"q": Xh[:, :, qs], "k": Xh[:, :, ks], "v": Xh[:, :, vs], "dout": dOh[:, :, qs]}
+        got = {"o": Ow[:, :, qs], "lse": lse, "dq": dX[:, :, qs], "dk": dX[:, :, ks], "dv": dX[:, :, vs]}
+        _check_rank(got, st, dtype, scale, True, f"packed {dtype} rank {r}")

@@ -112,9 +112,131 @@ def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _require(t, name: str):
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous device tensor")
+# ---------------------------------------------------------------------------- validation
+#
+# Every public call checks, before any ctypes call, that its tensors agree with q (or with
+# the relayout input) in shape, dtype and device.  A mis-shaped buffer would otherwise make
+# a kernel read or write past the end of an allocation.  The checks are pure Python over
+# shapes, dtypes and devices, so the CPU tests drive them with host tensors
+# (device_type="cpu").
+
+
+def _fail(msg: str):
+    raise ValueError(msg)
+
+
+def _same_place(ts, ref, names, device_type: str):
+    for t, n in zip(ts, names):
+        if t.device.type != device_type:
+            _fail(f"{n} must be a {device_type} tensor (got {t.device})")
+        if t.device != ref.device:
+            _fail(f"{n} is on {t.device}, q on {ref.device}")
+
+
+def _shape_is(t, shape, name: str):
+    if tuple(t.shape) != tuple(shape):
+        _fail(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype_is(t, dtype, name: str):
+    if t.dtype != dtype:
+        _fail(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _attn_dtype(q):
+    import torch
+
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        _fail(f"unsupported dtype {q.dtype} (bfloat16 or float32)")
+    return q.dtype
+
+
+def check_attn_fwd(q, k, v, out, lse, device_type: str = "cuda"):
+    """q [B,N,Hq,d]; k, v [B,N,Hkv,d]; out [B,N,Hq,d] (all one dtype); lse contiguous
+    float32 [B,Hq,N]; one device."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        _fail("q, k, v must be 4-d [B, N, H, d]")
+    B, N, Hq, d = q.shape
+    dt = _attn_dtype(q)
+    _shape_is(v, k.shape, "v")
+    _shape_is(k, (B, N, k.shape[2], d), "k")
+    _shape_is(out, (B, N, Hq, d), "out")
+    _shape_is(lse, (B, Hq, N), "lse")
+    for t, n in ((k, "k"), (v, "v"), (out, "out")):
+        _dtype_is(t, dt, n)
+    _dtype_is(lse, torch.float32, "lse")
+    if not lse.is_contiguous():
+        _fail("lse must be contiguous")
+    _same_place((q, k, v, out, lse), q, ("q", "k", "v", "out", "lse"), device_type)
+
+
+def check_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, device_type: str = "cuda"):
+    """The forward's checks for q, k, v, o, lse, plus dout and dq [B,N,Hq,d], dk and dv
+    [B,N,Hkv,d]."""
+    check_attn_fwd(q, k, v, o, lse, device_type)
+    dt = q.dtype
+    for t, n, like in ((dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+        _shape_is(t, like.shape, n)
+        _dtype_is(t, dt, n)
+    _same_place((dout, dq, dk, dv), q, ("dout", "dq", "dk", "dv"), device_type)
+
+
+def check_workspace(workspace, need: int, q, device_type: str = "cuda"):
+    """A contiguous uint8 workspace of at least `need` bytes on q's device."""
+    import torch
+
+    _dtype_is(workspace, torch.uint8, "workspace")
+    if not workspace.is_contiguous():
+        _fail("workspace must be contiguous")
+    if workspace.numel() < need:
+        _fail(f"workspace holds {workspace.numel()} bytes, {need} needed")
+    _same_place((workspace,), q, ("workspace",), device_type)
+
+
+def check_attn_varlen(q, k, v, out, lse, cu_seqlens, device_type: str = "cuda", grads=()):
+    """Packed sequences: q, out [T,Hq,d]; k, v [T,Hkv,d]; lse [Hq,T] float32; cu_seqlens a
+    1-d int32 table; every tensor contiguous and on q's device.  `grads` holds (dout, dq,
+    dk, dv) for the backward."""
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        _fail("varlen q, k, v must be 3-d [T, H, d]")
+    T, Hq, d = q.shape
+    dt = _attn_dtype(q)
+    _shape_is(k, (T, k.shape[1], d), "k")
+    _shape_is(v, k.shape, "v")
+    _shape_is(out, q.shape, "out")
+    _shape_is(lse, (Hq, T), "lse")
+    named = [(k, "k", dt), (v, "v", dt), (out, "out", dt), (lse, "lse", torch.float32)]
+    if grads:
+        dout, dq, dk, dv = grads
+        for t, n, like in ((dout, "dout", q), (dq, "dq", q), (dk, "dk", k), (dv, "dv", k)):
+            _shape_is(t, like.shape, n)
+            named.append((t, n, dt))
+    for t, n, want in named:
+        _dtype_is(t, want, n)
+    for t, n in [(q, "q")] + [(t, n) for t, n, _ in named]:
+        if not t.is_contiguous():
+            _fail(f"{n} must be contiguous")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        _fail("cu_seqlens must be a contiguous 1-d int32 tensor")
+    if cu_seqlens.numel() < 1:
+        _fail("cu_seqlens needs at least one entry")
+    _same_place([q] + [t for t, _, _ in named] + [cu_seqlens], q,
+                ["q"] + [n for _, n, _ in named] + ["cu_seqlens"], device_type)
+
+
+def check_relayout(x, out, out_shape, device_type: str = "cuda"):
+    """Relayout input and output: both contiguous, one dtype and device, out of `out_shape`."""
+    if not x.is_contiguous():
+        _fail("relayout input must be contiguous")
+    if not out.is_contiguous():
+        _fail("relayout output must be contiguous")
+    _shape_is(out, out_shape, "out")
+    _dtype_is(out, x.dtype, "out")
+    _same_place((x, out), x, ("input", "out"), device_type)
 
 
 def _tok_stride(t, name: str) -> int:
@@ -140,12 +262,14 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None,
     """
     import torch
 
+    if q.dim() != 4:
+        _fail("q must be 4-d [B, N, Hq, d]")
     B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
+    Hkv = k.shape[2] if k.dim() == 4 else 0
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     o = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device) if out is None else out
     lse_t = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _require(lse_t, "lse")
+    check_attn_fwd(q, k, v, o, lse_t)
     ts = [_tok_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "out"))]
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, N, Hq, Hkv, d)
     tail = (scale, int(causal), _dtype_code(q), _stream(stream))
@@ -154,6 +278,18 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None,
     else:
         _check("ul_attn_fwd_strided", lib().ul_attn_fwd_strided(*head, *ts, *tail))
     return o, lse_t
+
+
+def _internal_workspace(nbytes: int, device, stream):
+    """A workspace the binding allocates for one call.  When the call runs on a stream other
+    than the current one, the block is recorded on that stream, so the caching allocator
+    does not hand it out again before the kernels there are done with it."""
+    import torch
+
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
 
 
 def workspace_bytes(B, N, Hq, Hkv, d, dtype_code) -> int:
@@ -170,17 +306,20 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
     """
     import torch
 
-    _require(lse, "lse")
+    if q.dim() != 4 or k.dim() != 4:
+        _fail("q and k must be 4-d [B, N, H, d]")
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    code = _dtype_code(q)
-    need = workspace_bytes(B, N, Hq, Hkv, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device) if dq is None else dq
     dk = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dk is None else dk
     dv = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dv is None else dv
+    check_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv)
+    code = _dtype_code(q)
+    need = workspace_bytes(B, N, Hq, Hkv, d, code)
+    if workspace is None:
+        workspace = _internal_workspace(need, q.device, stream)
+    check_workspace(workspace, need, q)
     tensors = ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
                (dv, "dv"))
     ts = [_tok_stride(t, n) for t, n in tensors]
@@ -198,13 +337,6 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = T
     return dq, dk, dv
 
 
-def _require_table(cu):
-    import torch
-
-    if not cu.is_cuda or cu.dtype != torch.int32 or cu.dim() != 1 or not cu.is_contiguous():
-        raise ValueError("cu_seqlens must be a contiguous 1-d int32 device tensor")
-
-
 def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None,
                     causal: bool = True, out=None, lse=None, stream=None):
     """Attention over packed variable-length sequences.
@@ -214,16 +346,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = 
     """
     import torch
 
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, n)
-    _require_table(cu_seqlens)
+    if q.dim() != 3:
+        _fail("varlen q must be 3-d [T, Hq, d]")
     T, Hq, d = q.shape
-    Hkv = k.shape[1]
+    Hkv = k.shape[1] if k.dim() == 3 else 0
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
-    _require(o, "out")
-    _require(lse_t, "lse")
+    check_attn_varlen(q, k, v, o, lse_t, cu_seqlens)
     st = lib().ul_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), _ptr(cu_seqlens),
                                   cu_seqlens.numel() - 1, T, int(max_seqlen), Hq, Hkv, d, scale,
                                   int(causal), _dtype_code(q), _stream(stream))
@@ -237,21 +367,20 @@ def attn_bwd_varlen(q, k, v, o, dout, lse, cu_seqlens, max_seqlen: int,
     """dq, dk, dv of L = <dout, attn_fwd_varlen(q, k, v, ...)> (layouts as attn_fwd_varlen)."""
     import torch
 
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (lse, "lse")):
-        _require(t, n)
-    _require_table(cu_seqlens)
+    if q.dim() != 3 or k.dim() != 3:
+        _fail("varlen q and k must be 3-d [T, H, d]")
     T, Hq, d = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    code = _dtype_code(q)
-    need = workspace_bytes(1, T, Hq, Hkv, d, code)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _require(t, n)
+    check_attn_varlen(q, k, v, o, lse, cu_seqlens, grads=(dout, dq, dk, dv))
+    code = _dtype_code(q)
+    need = workspace_bytes(1, T, Hq, Hkv, d, code)
+    if workspace is None:
+        workspace = _internal_workspace(need, q.device, stream)
+    check_workspace(workspace, need, q)
     st = lib().ul_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                                   _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
                                   _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, int(max_seqlen), Hq,
@@ -264,11 +393,13 @@ def relayout_s2h(x, P: int, out=None, stream=None):
     """[C, N, H, d] sequence-sharded world view -> [C, P, N, H/P, d] head-sharded."""
     import torch
 
-    _require(x, "x")
+    if x.dim() != 4:
+        _fail("relayout input must be 4-d [C, N, H, d]")
     C, N, H, d = x.shape
     if P < 1 or H % P:
         raise ValueError("H must be a multiple of P")
     y = torch.empty((C, P, N, H // P, d), dtype=x.dtype, device=x.device) if out is None else out
+    check_relayout(x, y, (C, P, N, H // P, d))
     st = lib().ul_relayout_s2h(_ptr(x), _ptr(y), C, N, H, d, P, _dtype_code(x), _stream(stream))
     _check("ul_relayout_s2h", st)
     return y
@@ -278,9 +409,11 @@ def relayout_h2s(y, out=None, stream=None):
     """[C, P, N, H/P, d] head-sharded -> [C, N, H, d] sequence-sharded."""
     import torch
 
-    _require(y, "y")
+    if y.dim() != 5:
+        _fail("relayout input must be 5-d [C, P, N, H/P, d]")
     C, P, N, Hs, d = y.shape
     x = torch.empty((C, N, Hs * P, d), dtype=y.dtype, device=y.device) if out is None else out
+    check_relayout(y, x, (C, N, Hs * P, d))
     st = lib().ul_relayout_h2s(_ptr(y), _ptr(x), C, N, Hs * P, d, P, _dtype_code(y),
                                _stream(stream))
     _check("ul_relayout_h2s", st)
@@ -291,12 +424,13 @@ def relayout_s2h_heads(x, P: int, h0: int, Hc: int, out=None, stream=None):
     """[C, N, H, d] -> [C, P, N, Hc, d]: heads h0 .. h0+Hc-1 of every rank's slice."""
     import torch
 
-    _require(x, "x")
+    if x.dim() != 4:
+        _fail("relayout input must be 4-d [C, N, H, d]")
     C, N, H, d = x.shape
     if P < 1 or H % P:
         raise ValueError("H must be a multiple of P")
     y = torch.empty((C, P, N, Hc, d), dtype=x.dtype, device=x.device) if out is None else out
-    _require(y, "out")
+    check_relayout(x, y, (C, P, N, Hc, d))
     st = lib().ul_relayout_s2h_heads(_ptr(x), _ptr(y), C, N, H, d, P, h0, Hc, _dtype_code(x),
                                      _stream(stream))
     _check("ul_relayout_s2h_heads", st)
@@ -306,10 +440,11 @@ def relayout_s2h_heads(x, P: int, h0: int, Hc: int, out=None, stream=None):
 def relayout_h2s_heads(y, out, h0: int, stream=None):
     """Writes y [C, P, N, Hc, d] into heads h0 .. h0+Hc-1 of every rank's slice of `out`
     [C, N, H, d]; the other heads of `out` are left as they are.  Returns `out`."""
-    _require(y, "y")
-    _require(out, "out")
+    if y.dim() != 5 or out.dim() != 4:
+        _fail("head-chunk exchange: y must be [C, P, N, Hc, d] and out [C, N, H, d]")
     C, P, N, Hc, d = y.shape
     H = out.shape[2]
+    check_relayout(y, out, (C, N, H, d))
     st = lib().ul_relayout_h2s_heads(_ptr(y), _ptr(out), C, N, H, d, P, h0, Hc, _dtype_code(y),
                                      _stream(stream))
     _check("ul_relayout_h2s_heads", st)

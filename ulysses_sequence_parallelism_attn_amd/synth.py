@@ -8,8 +8,8 @@ Every tensor is drawn from ``numpy.random.Generator(PCG64(seed))`` as float64
 standard normals, narrowed to float32, and (for bf16 workloads) rounded to the
 nearest bf16 with ties to even.  The stored low-precision array *is* the input:
 the oracle widens exactly these values.  Seeds are ``1000 * workload + slot``
-with slot 1..7 for Q, K, V, dO, sampled rows, outlier keys and the relayout
-tensor.
+with slot 1..8 for Q, K, V, dO, sampled rows, outlier keys, the relayout
+tensor and sampled keys.
 
 The workloads are one Ulysses rank's share of a Llama-3.1-8B-shaped layer
 (32 query heads, 8 KV heads, head_dim 128) at SP = 4 or 8, plus a tiny fp32
@@ -24,7 +24,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-SLOT_Q, SLOT_K, SLOT_V, SLOT_DO, SLOT_ROWS, SLOT_OUTLIERS, SLOT_RELAYOUT = 1, 2, 3, 4, 5, 6, 7
+SLOT_Q, SLOT_K, SLOT_V, SLOT_DO, SLOT_ROWS, SLOT_OUTLIERS, SLOT_RELAYOUT, SLOT_KEYS = range(1, 9)
 
 # Normals drawn per chunk when generating very large tensors (bounds memory).
 _CHUNK = 1 << 24
@@ -59,6 +59,16 @@ class Workload:
     def flops_bwd(self) -> float:
         """Counted backward FLOPs: 10d per visible pair (2.5x the forward)."""
         return 2.5 * self.flops_fwd()
+
+    @property
+    def exchange(self) -> tuple:
+        """(C, N, H, d, P) of the QKV-stack exchange around this rank's attention: the
+        workload's own relayout case, else the full 32-head stack of the layer whose rank
+        share this is (P = 32 / Hq)."""
+        if self.relayout is not None:
+            return self.relayout
+        P = max(1, 32 // self.Hq)
+        return (3, self.N, self.Hq * P, self.d, P)
 
 
 WORKLOADS = {
@@ -164,6 +174,21 @@ def fixed_rows(N: int) -> np.ndarray:
     """Edge rows checked in addition to the sampled ones."""
     rows = [r for r in FIXED_ROWS if r < N] + [N // 2, N - 2, N - 1]
     return np.unique(np.array([r for r in rows if 0 <= r < N], dtype=np.int64))
+
+
+FIXED_KEYS = (0, 1, 127, 128)
+
+
+def sample_keys(wl: Workload, g: int, count: int = 512, window: int | None = None) -> np.ndarray:
+    """Sorted key positions of KV head g whose dK/dV rows are checked: `count` distinct keys
+    drawn uniformly from the last `window` positions (default: the whole sequence), plus the
+    fixed keys {0, 1, 127, 128, N/2} and the window's first and last keys."""
+    N = wl.N
+    lo = 0 if window is None else max(0, N - window)
+    rng = np.random.Generator(np.random.PCG64(seed_of(wl.wid, SLOT_KEYS) * 1000 + g))
+    drawn = lo + rng.choice(N - lo, size=min(count, N - lo), replace=False)
+    fixed = [x for x in FIXED_KEYS + (N // 2,) if lo <= x < N] + [lo, N - 1]
+    return np.unique(np.concatenate([drawn, np.array(fixed, dtype=np.int64)]))
 
 
 def random_bits(shape, dtype: str, seed: int) -> np.ndarray:
