@@ -1,19 +1,20 @@
 """The dK/dV producer's early barrier, checked on the compiled gfx950 code (CPU only).
 
 Before the barrier that hands its P / dS fragments to the consumers, a dK/dV producer waits
-only until its own P / dS writes have retired, and leaves the next step's operand reads in
-flight (`s_waitcnt lgkmcnt(K)` rather than lgkmcnt(0)).  That is exact only while the
-compiled code keeps three facts, which this test checks in the assembly of every kernel that
-contains the producer (the dK/dV kernels and the merged backward kernel, head_dim 64 and
-128):
-* between the last LDS write before the wait and the wait there are exactly K LDS reads and
-  no other LDS or scalar-memory operation;
+only until its own P / dS writes have retired, and leaves the LDS reads it issued after them
+in flight (`s_waitcnt lgkmcnt(K)` rather than lgkmcnt(0)).  That retires every write only
+while the compiled code keeps three facts, which this test checks in the assembly of every
+kernel that contains the producer (the dK/dV kernels and the merged backward kernel,
+head_dim 64 and 128):
+* between the last LDS write before the wait and the wait there are at least K LDS reads and
+  no other LDS or scalar-memory operation (LDS operations retire in order, so once at most K
+  are outstanding, everything before the last K reads, the writes included, has retired);
 * the wait is the instruction right before the barrier (so nothing touches LDS in between);
 * no scalar memory operation is issued after the kernel's first barrier (lgkmcnt then counts
-  LDS operations only, which retire in order).  This one is checked on the standalone dK/dV
-  kernels: the merged kernel also holds the dQ body, whose scalar loads are on a branch that
-  no dK/dV workgroup takes, while its dK/dV body is the same inlined code.
-K is the count the source defines, kKvAhead + kStatReads, read from the source.
+  LDS operations only).  This one is checked on the standalone dK/dV kernels: the merged
+  kernel also holds the dQ body, whose scalar loads are on a branch that no dK/dV workgroup
+  takes, while its dK/dV body is the same inlined code.
+K is the count the source defines, kReadsAfterPds, read from the source.
 """
 
 import re
@@ -53,11 +54,14 @@ LDS = re.compile(r"^ds_")
 SMEM = re.compile(r"^s_(load|buffer_load|store|buffer_store|atomic)")
 
 
+def _const(src, name):
+    """An integer constant of the source, following a definition by another constant's name."""
+    v = re.search(rf"constexpr int {name} = (\w+);", src).group(1)
+    return int(v) if v.isdigit() else _const(src, v)
+
+
 def _expected_count():
-    src = (CSRC / "attn_bwd.hip").read_text()
-    ahead = int(re.search(r"constexpr int kKvAhead = (\d+);", src).group(1))
-    stat = re.search(r"constexpr int kStatReads = ([\d *+-]+);", src).group(1)
-    return ahead + eval(stat, {"__builtins__": {}})
+    return _const((CSRC / "attn_bwd.hip").read_text(), "kReadsAfterPds")
 
 
 def test_producer_waits_retire_exactly_the_pds_writes(asm):
@@ -74,20 +78,23 @@ def test_producer_waits_retire_exactly_the_pds_writes(asm):
         for i in waits:
             k = K
             j = i
-            while j > 0 and not ins[j].startswith("ds_write"):
+            while j > 0 and not ins[j].startswith(("ds_write", "s_barrier")):
                 j -= 1
             if not ins[j].startswith("ds_write"):
-                continue
+                continue  # no LDS write since the previous barrier: not a producer hand-over
             between = ins[j + 1:i]
             reads = [x for x in between if x.startswith("ds_read")]
             others = [x for x in between if (LDS.match(x) and not x.startswith("ds_read")) or SMEM.match(x)]
-            assert len(reads) == k and not others, (name, i, k, len(reads), others)
+            assert len(reads) >= k and not others, (name, i, k, len(reads), others)
             n = i + 1
             while not ins[n].startswith("s_barrier"):
                 assert not LDS.match(ins[n]) and not SMEM.match(ins[n]), (name, ins[n])
                 n += 1
             checked += 1
-        assert checked >= 6, (name, checked)  # one per unrolled producer step
+        # one per unrolled producer iteration; the compiler may peel the first iteration,
+        # whose stores (P = dS = 0 over LDS that is already zero) it can drop, leaving that
+        # barrier with no hand-over to check
+        assert checked >= 5, (name, checked)
         if "dq_dkdv" not in name:
             first_barrier = next(i for i, x in enumerate(ins) if x.startswith("s_barrier"))
             assert not any(SMEM.match(x) for x in ins[first_barrier:]), name

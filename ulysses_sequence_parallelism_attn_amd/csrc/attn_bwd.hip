@@ -10,9 +10,10 @@
 //   dk_j = scale sum_{h in group, i} ds_ij q_i,  dv_j = sum_{h in group, i} p_ij dO_i.
 //
 // Three launches on the caller's stream, no atomics (bit-reproducible):
-//  1. pre:   -D = -rowsum(dO * O) and lse in log2 units -> workspace (fp32).
-//            D is stored negated so that dP - D can start as the dP
-//            MFMA's accumulator (see dkdv_sdp).
+//  1. pre:   -lse/scale and -D = -rowsum(dO * O) -> workspace (fp32).  Both
+//            are stored as the starting values of MFMA accumulators: S + (-lse
+//            / scale) scaled by scale log2(e) is the exponent of P in base 2,
+//            and dP + (-D) is what dS multiplies.
 //  2. dq:    per (b, KV head, query block), like the forward: streams K/V
 //            tiles, recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T and
 //            accumulates dQ^T += K^T dS^T in registers.
@@ -40,8 +41,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // ============================================================================ pre kernel
 
-// Workspace layout: for each (b, h), N floats of lse2 (= lse log2 e) then N
-// floats of -D, so both statistics of a query tile are one block apart.
+// Workspace layout: for each (b, h), N floats of -lse/scale then N floats of
+// -D, so both statistics of a query tile are one block apart.
 struct PreParams {
     const void *o, *dout;
     const float *lse;
@@ -50,6 +51,7 @@ struct PreParams {
     int64_t o_rs, do_rs;  // elements between consecutive tokens of o and of dout
     int32_t B, Hq, d;
     int32_t is_bf16;
+    float scale;
 };
 
 // L lanes per (b, i, h) row, each with one 16-byte load of o and one of dout
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreParams p) {
         const int64_t bi = row / p.Hq;
         const int64_t i = bi % p.N, b = bi / p.N;
         const int64_t bh = b * p.Hq + h;
-        p.stats[(2 * bh) * p.N + i] = p.lse[bh * p.N + i] * kLog2e;
+        p.stats[(2 * bh) * p.N + i] = -(p.lse[bh * p.N + i] / p.scale);
         p.stats[(2 * bh + 1) * p.N + i] = -acc;
     }
 }
@@ -221,11 +223,12 @@ __device__ __forceinline__ void dq_prefetch(bf16x8 (&ring)[kQAhead<D>], uint32_t
     }
 }
 
-// dS^T = P^T (dP^T - D) with P^T = exp2(S^T c - lse2), as two bf16 B
-// fragments of 16 keys; `dpd` already holds dP^T - D (dq_gemm).  MASK zeroes
-// P past the causal diagonal and the ragged end.
+// dS^T = P^T (dP^T - D) with P^T = exp2(S^T c + cn), cn = -(lse/scale) c =
+// -lse log2(e), as two bf16 B fragments of 16 keys; `dpd` already holds
+// dP^T - D (dq_gemm).  MASK zeroes P past the causal diagonal and the ragged
+// end.
 template <bool MASK>
-__device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f32x16 &dpd, float lse2,
+__device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f32x16 &dpd, float cn,
                                       int kg, int j0, int row, int N, int causal, float c) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -233,7 +236,7 @@ __device__ __forceinline__ void dq_ds(bf16x8 (&dsf)[2], const f32x16 &s, const f
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int r = hh * 8 + q;
-            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+            float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, cn));
             if constexpr (MASK) {
                 const int j = j0 + ckey(r, kg);
                 if (j >= N || (causal && j > row)) pv = 0.f;
@@ -289,8 +292,8 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
                                : u32x4{0, 0, 0, 0});
     }
     const int64_t so = sq.st0 + (int64_t)h * 2 * sq.hs + (ok ? row : 0);
-    const float lse2 = ok ? p.stats[so] : 0.f;
-    const float nDrow = ok ? p.stats[so + sq.hs] : 0.f;  // -D
+    const float cn = ok ? p.stats[so] * p.scale_log2 : 0.f;  // -lse log2(e)
+    const float nDrow = ok ? p.stats[so + sq.hs] : 0.f;     // -D
     f32x16 nd;  // the dP^T accumulator's starting value
 #pragma unroll
     for (int r = 0; r < 16; ++r) nd[r] = nDrow;
@@ -400,9 +403,9 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         __builtin_amdgcn_sched_barrier(0);
         if (FULL || (t < ntiles && visible(t))) {
             if constexpr (FULL)
-                dq_ds<false>(dsf, s, dp, lse2, kg, t * kDqKT, row, N, p.causal, c);
+                dq_ds<false>(dsf, s, dp, cn, kg, t * kDqKT, row, N, p.causal, c);
             else
-                dq_ds<true>(dsf, s, dp, lse2, kg, t * kDqKT, row, N, p.causal, c);
+                dq_ds<true>(dsf, s, dp, cn, kg, t * kDqKT, row, N, p.causal, c);
             dq_prefetch<D>(ring, stage(t), fo);
         }
         fence_barrier();
@@ -447,23 +450,31 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 // waves 4-7 consumers, and producer w shares a SIMD with consumer w+4.  The
 // workgroup steps over 32-row query tiles of every query head of the group,
 // from the end of the sequence down to the causal diagonal.
-//   producer w, step i:  for its 32 keys, S = Q K^T and dP = dO V^T  (A = Q /
+//   producer w, step t:  for its 32 keys, S = Q K^T and dP = dO V^T  (A = Q /
 //                        dO rows from LDS, B = K / V fragments held in
-//                        registers), P = exp2(S c - lse2), dS = P (dP - D);
+//                        registers), P = exp2(S c - lse log2 e), dS = P (dP - D);
 //                        the bf16 P and dS fragments go to LDS in the lane
 //                        order of a B operand.
-//   consumer c, step i-1: for keys 64 (c/2) .. +64 and head dims 64 (c%2) ..
+//   consumer c, step t:  for keys 64 (c/2) .. +64 and head dims 64 (c%2) ..
 //                        +64, dV^T += dO^T P and dK^T += Q^T dS  (A = dO^T / Q^T
 //                        by transposed LDS reads, B = the producers' P / dS),
 //                        summed over the group's heads.  Each A fragment feeds
-//                        the MFMAs of two 32-key blocks, which halves the
-//                        consumers' LDS reads against one 32-key block each.
-// Each step has two halves split by a barrier: in the first the producers
-// issue their 16 MFMAs while the consumers read their operands; in the second
-// the consumers issue their 16 MFMAs (with the tile loads between them) while
-// the producers do the softmax VALU work, store P / dS and read the next
-// step's operands.  Each role fits in 256 registers (2 waves per SIMD).  Q/dO
-// tiles rotate through 6 LDS stages (steps i-1 .. i+4), P/dS through 2.
+//                        the MFMAs of two 32-key blocks.
+// One barrier per iteration, and in iteration t all three stages of the
+// pipeline run at once, so that the matrix pipe of every SIMD always has a
+// wave with MFMAs to issue:
+//   * the producer issues the 16 MFMAs of step t (S and dP) and, one element
+//     per MFMA, the softmax of step t-1 (whose S and dP it kept in a second
+//     accumulator set), storing P / dS of step t-1;
+//   * the consumer issues the 16 MFMAs of step t-2 on the P / dS that the
+//     producer stored in the previous iteration, and the tile loads of step
+//     t+3.
+// The producer needs no statistics registers and no mask branch in its
+// softmax: the S accumulator of a step starts from -lse/scale of its row
+// (or -inf where the key is masked: past the row, past N), the dP
+// accumulator from -D, so that P = exp2(c * S) and dS = P * dP.  Each role
+// fits in 256 registers (2 waves per SIMD).  Q/dO tiles (and the rows'
+// statistics) rotate through 6 LDS stages, P/dS through 2 buffers.
 
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
@@ -472,6 +483,11 @@ constexpr int kKeysPerWave = 32;                     // keys of one producer
 constexpr int kKeysPerWg = kKvPairs * kKeysPerWave;  // 128
 constexpr int kQT = 32;                              // query rows per step
 constexpr int kKvAhead = 6;                          // A fragments read ahead of their MFMA
+// LDS reads a producer issues between its last P/dS write of a step and the
+// hand-over barrier: the kKvAhead first fragments of the next step.  The wait
+// before the barrier lets this many stay outstanding, which retires every
+// write before them.
+constexpr int kReadsAfterPds = kKvAhead;
 
 struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
@@ -492,11 +508,11 @@ struct DkvParams {
 template <int D>
 struct DkvTile {
     static constexpr int kBytes = kQT * D * 2;                  // one Q or dO tile
-    static constexpr int kAhead = 5;                            // steps from a load to its use
-    static constexpr int kStages = kAhead + 1;                  // steps i-1 .. i+kAhead-1
-    static_assert(kStages % 2 == 0, "P/dS buffer parity follows the stage index");
+    static constexpr int kStages = 6;                           // steps t-2 .. t+3
+    static constexpr int kAhead = kStages - 3;                  // iterations from a load to its step
+    static_assert(kStages % 2 == 0, "P/dS buffer parity follows the unrolled iteration index");
     static constexpr int kDoBase = kStages * kBytes;
-    static constexpr int kStatBytes = 2 * kQT * 4;              // lse2 then D, fp32
+    static constexpr int kStatBytes = 2 * kQT * 4;              // -lse/scale then -D, fp32
     static constexpr int kStatBase = 2 * kStages * kBytes;
     static constexpr int kPdsPair = 4 * 64 * 16;                // P[2], dS[2] fragments of one producer
     static constexpr int kPds = kKvPairs * kPdsPair;            // one buffer
@@ -509,12 +525,8 @@ struct DkvTile {
 
 // ---- producer
 
-// S and dP of one step as a stream of 2 KK MFMAs, the KK of S first, then
-// those of dP (A = Q / dO row fragments of the tile at stage offset `qst`), so
-// that S is complete well before the softmax needs it (measured: 1.4-2 %
-// faster than alternating them, 3.5 % faster than dP first); the first
-// kKvAhead fragments are already in `ring` (read at the end of the previous
-// step).
+// A fragment `st` of a step's MFMA stream: the KK fragments of S first (Q
+// rows), then those of dP (dO rows), of the tile at stage offset `qst`.
 template <int D>
 __device__ __forceinline__ bf16x8 dkdv_sdp_frag(int st, uint32_t qst, const uint32_t *oq, const uint32_t *od) {
     constexpr int KK = D / 16;
@@ -528,79 +540,84 @@ __device__ __forceinline__ void dkdv_sdp_prefetch(bf16x8 (&ring)[kKvAhead], uint
     for (int st = 0; st < kKvAhead; ++st) ring[st] = dkdv_sdp_frag<D>(st, qst, oq, od);
 }
 
-// `side(k)`, k < NSIDE, runs between MFMAs spread over the stream (the tile
-// loads).
-// dP starts from `nd` (-D of each C register's row), so the stream leaves
-// dP - D in `dp` and the softmax saves a subtraction per element.
-template <int D, int NSIDE, typename Side>
-__device__ __forceinline__ void dkdv_sdp(f32x16 &s, f32x16 &dp, const f32x16 &nd, const bf16x8 *kf,
-                                         const bf16x8 *vf, bf16x8 (&ring)[kKvAhead], uint32_t qst,
-                                         const uint32_t *oq, const uint32_t *od, Side &&side) {
-    constexpr int NSTEP = 2 * (D / 16), EVERY = NSTEP / NSIDE;
-    s = zero16();
-    dp = nd;
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-        const bf16x8 a = ring[st % kKvAhead];
-        if (st + kKvAhead < NSTEP) ring[st % kKvAhead] = dkdv_sdp_frag<D>(st + kKvAhead, qst, oq, od);
-        constexpr int KK = D / 16;
-        if (st < KK)
-            s = mfma32x32x16(a, kf[st], s);
-        else
-            dp = mfma32x32x16(a, vf[st - KK], dp);
-        if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// The statistics of this lane group's 16 rows (the 8-row runs hh, rows 0-3
-// then 4-7 of each), read from a stage's block at `stat`: lse2 by run, and
-// -D as one register block in C order (register hh*8 + x*4 + q), the dP
-// accumulator's starting value.
-struct DkvStats {
-    f32x4 l[2][2];
-    f32x16 nd;
-};
-
-constexpr int kStatReads = 2 * 2 * 2;  // LDS reads (one 16-byte read each) in dkdv_stats
-__device__ __forceinline__ void dkdv_stats(DkvStats &t, uint32_t stat) {
-    f32x4 d[2][2];
+// The starting values of step t+1's accumulators for this lane's 16 rows
+// (C register r holds row ckey(r, kg): two runs of 8 consecutive rows,
+// 16*hh + 8*kg ..), read from a stage's statistics block at `stat`: -lse/scale
+// into `sinit`, -D into `ninit`, both in C-register order.
+__device__ __forceinline__ void dkdv_inits(f32x16 &sinit, f32x16 &ninit, uint32_t stat) {
+    f32x4 l[2][2], d[2][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            t.l[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + hh * 64 + x * 16));
+            l[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + hh * 64 + x * 16));
             d[hh][x] = *reinterpret_cast<const UL_LDS f32x4 *>((uintptr_t)(stat + kQT * 4 + hh * 64 + x * 16));
         }
+    const f32x8 l0 = __builtin_shufflevector(l[0][0], l[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x8 l1 = __builtin_shufflevector(l[1][0], l[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
+    sinit = __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     const f32x8 d0 = __builtin_shufflevector(d[0][0], d[0][1], 0, 1, 2, 3, 4, 5, 6, 7);
     const f32x8 d1 = __builtin_shufflevector(d[1][0], d[1][1], 0, 1, 2, 3, 4, 5, 6, 7);
-    t.nd = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    ninit = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 }
 
-// P = exp2(S c - lse2) (zero where MASK finds a key past the row or past N)
-// and dS = P (dP - D) as bf16 B fragments at this lane's slot `pds`; `dpd`
-// already holds dP - D (dkdv_sdp).  C register r of lane group kg holds
-// query row ckey(r, kg): two runs of 8 consecutive rows (16*hh + 8*kg ..),
-// whose lse2 values are in `t`.
-template <bool MASK>
-__device__ __forceinline__ void dkdv_softmax(const f32x16 &s, const f32x16 &dpd, const DkvStats &t, uint32_t pds,
-                                             int kg, int r0, int key, int N, int causal, float c) {
+// Masked step (rows r0 .. r0+31 against this lane's key): the S accumulator
+// starts at -inf where the key is not visible to the row or either lies past
+// N, so P = exp2(-inf) = 0 there.
+__device__ __forceinline__ void dkdv_mask_init(f32x16 &sinit, int kg, int r0, int key, int N, int causal) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 l0 = t.l[hh][0], l1 = t.l[hh][1];
-        float pv[8], ds[8];
+    for (int r = 0; r < 16; ++r) {
+        const int i = r0 + ckey(r, kg);
+        sinit[r] = (i >= N || key >= N || (causal && key > i)) ? -INFINITY : sinit[r];
+    }
+}
+
+// One producer iteration: the MFMA stream of step t into (sa, dpa), whose
+// starting values (-lse/scale or -inf, and -D) they already hold, with A
+// fragments from the tile at stage offset `qst` (the first kKvAhead already in
+// `ring`).  Between the MFMAs runs the softmax of step t-1 from (sb, dpb),
+// software-pipelined so that the VALU work after each MFMA has no dependency
+// inside it: element e's exponent argument c * s, two elements' worth of the
+// exp2 and of the product dS = p * dp trail by one MFMA each (at D = 64 two
+// elements per MFMA).  P and dS go to `pds` as bf16 B fragments (P of the
+// lane's rows 0-7 / 8-15, then dS) as soon as 8 of them are done.  `mid()` runs
+// halfway through the stream (it loads the next step's starting values).
+template <int D, typename Mid>
+__device__ __forceinline__ void dkdv_producer_iter(f32x16 &sa, f32x16 &dpa, const f32x16 &sb, const f32x16 &dpb,
+                                                   const bf16x8 *kf, const bf16x8 *vf, bf16x8 (&ring)[kKvAhead],
+                                                   uint32_t qst, const uint32_t *oq, const uint32_t *od,
+                                                   uint32_t pds, float c, Mid &&mid) {
+    constexpr int KK = D / 16, NSTEP = 2 * KK, EPB = 16 / NSTEP;
+    static_assert(16 % NSTEP == 0, "softmax elements spread evenly over the MFMAs");
+    float arg[16], pv[16], ds[16];
+    auto write_half = [&](int hh) {
+        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + hh * 64 * 16)) =
+            __builtin_bit_cast(u32x4, pack8(pv + 8 * hh));
+        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + (2 + hh) * 64 * 16)) =
+            __builtin_bit_cast(u32x4, pack8(ds + 8 * hh));
+    };
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int r = hh * 8 + q;
-            pv[q] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -(q < 4 ? l0[q] : l1[q - 4])));
-            if constexpr (MASK) {
-                const int i = r0 + ckey(r, kg);
-                pv[q] = (i >= N || key >= N || (causal && key > i)) ? 0.f : pv[q];
-            }
-            ds[q] = pv[q] * dpd[r];
+    for (int e = 0; e < EPB; ++e) arg[e] = c * sb[e];
+#pragma unroll
+    for (int st = 0; st <= NSTEP; ++st) {
+        if (st < NSTEP) {
+            const bf16x8 a = ring[st % kKvAhead];
+            if (st + kKvAhead < NSTEP) ring[st % kKvAhead] = dkdv_sdp_frag<D>(st + kKvAhead, qst, oq, od);
+            if (st < KK)
+                sa = mfma32x32x16(a, kf[st], sa);
+            else
+                dpa = mfma32x32x16(a, vf[st - KK], dpa);
         }
-        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + hh * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(pv));
-        *reinterpret_cast<UL_LDS u32x4 *>((uintptr_t)(pds + (2 + hh) * 64 * 16)) = __builtin_bit_cast(u32x4, pack8(ds));
+#pragma unroll
+        for (int e = 0; e < EPB; ++e) {
+            const int r = st * EPB + e;  // this block: arg of r + EPB, exp of r, dS of r - EPB
+            if (r + EPB < 16) arg[r + EPB] = c * sb[r + EPB];
+            if (r < 16) pv[r] = __builtin_amdgcn_exp2f(arg[r]);
+            if (r >= EPB) ds[r - EPB] = pv[r - EPB] * dpb[r - EPB];
+        }
+        if (st >= 1 && (st * EPB) % 8 == 0) write_half(st * EPB / 8 - 1);
+        if (st == KK) mid();
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -645,9 +662,11 @@ struct DkdvCons {
                 else
                     dkacc[e2][kb2] = mfma32x32x16(a, db[kb2][ks], dkacc[e2][kb2]);
             }
+            if constexpr (NSIDE > 0) {
 #pragma unroll
-            for (int k = 0; k < NSIDE; ++k)
-                if (k * NA / NSIDE == st) side(k);
+                for (int k = 0; k < NSIDE; ++k)
+                    if (k * NA / NSIDE == st) side(k);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -702,26 +721,24 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     };
     const Cur first{0, 0, (nqt - 1) * kQT};
 
-    // Zero the LDS: the step before the first reads never-loaded stage and
-    // P/dS memory, which must hold zeros (P = dS = 0 contribute nothing).
+    // Zero the LDS: the first two iterations' consumers read never-written
+    // stage and P/dS memory, which must hold zeros (P = dS = 0 contribute
+    // nothing).
     for (int x = tid; x < T::kLds / 16; x += kKvThreads)
         *reinterpret_cast<UL_LDS u32x4 *>(lds + x * 16) = u32x4{0, 0, 0, 0};
     __builtin_amdgcn_s_waitcnt(0xc07f);
     fence_barrier();
 
-    // Step halves for i = 0 .. nsteps (unrolled by the stage count so stage
-    // offsets are constants): stage i % 6 holds step i's tiles, P/dS buffer
-    // i % 2 its fragments.  Every step runs in full: where a producer's keys
-    // see none of a step's rows the mask makes P and dS zero, and the
-    // iteration past the last step works on a re-read of the last step's
-    // tiles (finite, unused).
-    auto run = [&](auto half_a, auto half_b) {
-        for (int i0 = 0; i0 <= nsteps; i0 += T::kStages) {
+    // Iterations t = 0 .. nsteps+1, unrolled by the stage count so that every
+    // stage offset and buffer parity is a constant: step t's tiles and
+    // statistics sit in stage t % 6, its P/dS in buffer t % 2.  Past the last
+    // step the producer works on re-reads of the last step's tiles with every
+    // element masked, and what it stores is never read.
+    const int niter = nsteps + 2;
+    auto run = [&](auto iter) {
+        for (int i0 = 0; i0 < niter; i0 += T::kStages) {
             [&]<int... J>(std::integer_sequence<int, J...>) {
-                ((i0 + J <= nsteps ? (half_a(i0 + J, std::integral_constant<int, J>{}),
-                                      half_b(i0 + J, std::integral_constant<int, J>{}))
-                                   : void()),
-                 ...);
+                ((i0 + J < niter ? iter(std::integral_constant<int, J>{}) : void()), ...);
             }(std::make_integer_sequence<int, T::kStages>{});
         }
     };
@@ -761,53 +778,69 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         asm volatile("" : "+v"(pds));
         const float c = p.scale_log2;
 
-        fence_barrier();  // the consumers' first loads have landed
-        bf16x8 ring[kKvAhead];
-        f32x16 s, dp;
-        DkvStats stats;
-        // The producer needs only each step's first row: r0 drops by a tile
-        // every grp steps.  Masked steps are those with r0 below mlo (the
-        // causal diagonal) or above mhi (the ragged end), and every step when
-        // the key block runs past N.  Past the last step r0 keeps dropping;
-        // that iteration's P / dS are masked and never used, and the
-        // producer addresses no memory with r0.
+        // A step is masked when its rows reach below mlo (the causal diagonal)
+        // or above mhi (the ragged end), when the key block runs past N, and
+        // for every step past the last one (`left` counts the steps still to
+        // be prepared).  The producer needs only each step's first row: it
+        // drops by a tile every grp steps.
         const int mlo = kb0 + kKeysPerWg > N ? INT_MAX : (p.causal ? kb0 + kKeysPerWg : INT_MIN);
         const int mhi = N - kQT;
-        int r0 = first.r0, hc = grp;
-        dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
-        dkdv_stats(stats, stat + T::stat_stage(0));
-        run(
-            [&](int, auto stage) {  // MFMA half: S and dP of step i
-                constexpr int ST = decltype(stage)::value;
-                dkdv_sdp<D, 1>(s, dp, stats.nd, kf, vf, ring, T::q_stage(ST), oq, od, [](int) {});
-                fence_barrier();
-            },
-            [&](int, auto stage) {  // P / dS of step i, then step i+1's operands
-                constexpr int ST = decltype(stage)::value, NX = (ST + 1) % T::kStages;
-                if (r0 < mlo || r0 > mhi)
-                    dkdv_softmax<true>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
-                else
-                    dkdv_softmax<false>(s, dp, stats, pds + (ST % 2) * T::kPds, kg, r0, key, N, p.causal, c);
-                if (--hc == 0) {
-                    hc = grp;
-                    r0 -= kQT;
+        int r0 = first.r0, hc = grp, left = nsteps;
+        auto prepare = [&](f32x16 &sinit) {  // mask the S starting values of the step at (r0, left)
+            if (left <= 0 || r0 < mlo || r0 > mhi) {
+                if (left <= 0) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sinit[r] = -INFINITY;
+                } else {
+                    dkdv_mask_init(sinit, kg, r0, key, N, p.causal);
                 }
-                dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
-                dkdv_stats(stats, stat + T::stat_stage(NX));
-                // P / dS stored before the barrier; the next step's operand
-                // reads may stay in flight across it (they are waited for
-                // at their first use).  LDS operations retire in order, the
-                // loop issues no scalar memory operation, and after the last
-                // P / dS write exactly kKvAhead fragment reads and
-                // kStatReads statistics reads follow (16-byte reads of
-                // distinct addresses, which the compiler cannot merge), so
-                // waiting until at most that many are outstanding retires
-                // exactly the writes.
-                constexpr int kReadsAfterPds = kKvAhead + kStatReads;
-                static_assert(kReadsAfterPds < 15, "lgkmcnt immediate (15 encodes no wait)");
-                __builtin_amdgcn_s_waitcnt(0xc07f | (kReadsAfterPds << 8));
-                fence_barrier();
-            });
+            }
+        };
+        auto next_step = [&]() {
+            --left;
+            if (--hc == 0) {
+                hc = grp;
+                r0 -= kQT;
+            }
+        };
+
+        fence_barrier();  // the consumers' first loads have landed
+        // Set 0 starts as step 0; set 1 holds "step -1": P = exp2(-inf) = 0, dS = 0.
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            s[1][r] = -INFINITY;
+            dp[1][r] = 0.f;
+        }
+        bf16x8 ring[kKvAhead];
+        dkdv_inits(s[0], dp[0], stat + T::stat_stage(0));
+        prepare(s[0]);
+        dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
+        run([&](auto J) {
+            constexpr int ST = decltype(J)::value;          // stage of step t
+            constexpr int A = ST % 2, Bs = (ST + 1) % 2;    // accumulator sets of steps t and t-1 (then t+1)
+            constexpr int NX = (ST + 1) % T::kStages;       // stage of step t+1
+            constexpr int PB = (ST + 1) % 2;                // P/dS buffer of step t-1
+            f32x16 sn, nn;  // starting values of step t+1, loaded halfway through the stream
+            dkdv_producer_iter<D>(s[A], dp[A], s[Bs], dp[Bs], kf, vf, ring, T::q_stage(ST), oq, od,
+                                  pds + PB * T::kPds, c,
+                                  [&]() { dkdv_inits(sn, nn, stat + T::stat_stage(NX)); });
+            s[Bs] = sn;
+            dp[Bs] = nn;
+            next_step();
+            prepare(s[Bs]);
+            dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
+            // P / dS of step t-1 stored before the barrier; the next step's
+            // operand reads may stay in flight across it (they are waited for
+            // at their first use).  LDS operations retire in order, the loop
+            // issues no scalar memory operation, and after the last P / dS
+            // write only LDS reads follow (16-byte reads of distinct addresses,
+            // which the compiler cannot merge): the kKvAhead first fragments
+            // of step t+1.  Waiting until at most that many are outstanding
+            // retires the writes.
+            __builtin_amdgcn_s_waitcnt(0xc07f | (kReadsAfterPds << 8));
+            fence_barrier();
+        });
         return;
     }
 
@@ -816,8 +849,8 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // Direct loads of a step into its LDS stage, issued between the
     // consumers' MFMAs: the Q and dO tiles are split evenly over the 4
     // consumers (each one's share inside one of the two); the last consumer
-    // also fetches the 32 lse2 and D values, one dword per lane.  Rows past N
-    // re-read row N-1 (masked by the producers).
+    // also fetches the 32 rows' -lse/scale and -D, one dword per lane.  Rows
+    // past N re-read row N-1 (masked by the producers).
     constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvPairs;
     static_assert(2 * Tile::INSTR % kKvPairs == 0 && Tile::INSTR % kDmaPerWave == 0,
                   "Q and dO tiles split evenly over the consumers");
@@ -834,52 +867,65 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
     }
     const bool stats_wave = pair == kKvPairs - 1;
-    // load k of this consumer's share of step `cu` into stage st (k =
-    // kDmaPerWave: the statistics, on the last consumer)
-    auto issue_k = [&](const Cur &cu, int st, int k) {
+    // The loads of a step, issued together: this consumer's share of the Q or
+    // dO tile of step `cu` into stage st, and on the last consumer the 32
+    // rows' -lse/scale (lanes 0-31) and -D (lanes 32-63, one statistics block
+    // later), one dword per lane.  `trow` / `srow` point at head 0 of the
+    // group at the step's first row; head hi adds hi * D elements (hi * 2 hs
+    // statistics).  Rows past N re-read row N-1 (masked by the producers).
+    const int64_t head_stride_st = 2 * sq.hs;
+    // load k of the step (k = kDmaPerWave: the statistics, last consumer only)
+    auto issue_k = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st, int k) {
         const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
-        const int h = g * grp + cu.hi;
         if (k < kDmaPerWave) {
-            const uint16_t *tb = tens + (sq.tok0 + cu.r0) * t_rs + (int64_t)h * D;
-            dma_b128(tb, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
-                     lds + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
-        } else if (stats_wave) {
-            // lanes 0..31 read the lse2 rows, lanes 32..63 the D rows one
-            // statistics block later (each lane lands at its own dword of the
-            // stage's block)
-            const float *sl = p.stats + sq.st0 + (int64_t)h * 2 * sq.hs + cu.r0;
+            dma_b128_m0(trow + cu.hi * D, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
+                        lbase + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
+        } else if (stats_wave) {  // two loads, one per half of the wave, each from a uniform base
+            const float *sl = srow + cu.hi * head_stride_st;
             const int r = min(lane & (kQT - 1), lim);
+            const uint32_t sdst = lbase + T::kStatBase + T::stat_stage(st);
             if (lane < kQT)
-                dma_b32(sl, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
+                dma_b32_m0(sl, (uint32_t)r * 4, sdst);
             else
-                dma_b32(sl + sq.hs, (uint32_t)r * 4, lds + T::kStatBase + T::stat_stage(st));
+                dma_b32_m0(sl + sq.hs, (uint32_t)r * 4, sdst);
         }
     };
-    auto issue = [&](const Cur &cu, int st) {
+    auto issue = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st) {
 #pragma unroll
-        for (int k = 0; k <= kDmaPerWave; ++k) issue_k(cu, st, k);
+        for (int k = 0; k <= kDmaPerWave; ++k) issue_k(cu, trow, srow, st, k);
     };
-    // Loads run kAhead steps ahead (past the last step they re-read it into
-    // a free stage), so every consumer has the same number in flight at each
-    // wait.  The MFMA half of step i issues step i+kAhead-1; before the
-    // barrier ending the first half of step i (which follows the loads of
-    // step i+kAhead-2) step i+1 must have landed: all but the newest kAhead-3
-    // steps' worth.
-    // The operand reads of the first half need not retire before its
-    // barrier: their registers are waited for at the MFMAs that use them,
-    // and the memory they read is rewritten two barriers later at the
-    // earliest (P/dS buffer i % 2 by the producers' half of step i+1, the
-    // Q/dO stage by the loads issued in the second half of step i+1).
+    // Loads run kAhead = 3 iterations ahead (past the last step they re-read
+    // it into a free stage), so every consumer has the same number in flight
+    // at each wait.  Iteration t issues step t+3; before the barrier ending
+    // it, step t+2 must have landed (the producer reads its statistics and
+    // first fragments in iteration t+1): all but this iteration's loads.
+    // A stage is rewritten three iterations after the consumers' last read
+    // of it (step t-3's stage takes step t+3; step t-3 was consumed in
+    // iteration t-1, whose reads its MFMAs waited for).
     auto wait_next = [&]() {
         if (stats_wave)
-            wait_vm_only<(T::kAhead - 3) * (kDmaPerWave + 2)>();
+            wait_vm_only<kDmaPerWave + 2>();
         else
-            wait_vm_only<(T::kAhead - 3) * kDmaPerWave>();
+            wait_vm_only<kDmaPerWave>();
+    };
+    // The cursor of the step to load next, with its row pointers.
+    const uint16_t *trow0 = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)g * grp * D;
+    const float *srow0 = p.stats + sq.st0 + (int64_t)g * grp * head_stride_st + first.r0;
+    const int64_t trow_step = (int64_t)kQT * t_rs;
+    auto advance_load = [&](Cur &cu, const uint16_t *&trow, const float *&srow) {
+        const int r0 = cu.r0;
+        advance(cu);
+        if (cu.r0 != r0) {
+            trow -= trow_step;
+            srow -= kQT;
+        }
     };
     Cur iss = first;
+    const uint16_t *trow = trow0;
+    const float *srow = srow0;
     [&]<int... J>(std::integer_sequence<int, J...>) {
-        ((issue(iss, J), advance(iss)), ...);
-    }(std::make_integer_sequence<int, T::kAhead - 1>{});
+        ((issue(iss, trow, srow, J), advance_load(iss, trow, srow)), ...);
+    }(std::make_integer_sequence<int, T::kAhead>{});
     wait_vm<0>();  // the first steps have landed
     fence_barrier();
 
@@ -911,29 +957,27 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             dkacc[e2][k2] = zero16();
         }
     bf16x8 ring[Cons::AH], pb[2][2], db[2][2];
-    run(
-        [&](int, auto stage) {  // operands of step i-1; step i+1 landed
-            constexpr int ST = decltype(stage)::value, PV = (ST + T::kStages - 1) % T::kStages;
-            const uint32_t buf = pds + (PV % 2) * T::kPds;
+    cons.prefetch(ring, T::q_stage(T::kStages - 2));  // step -2 (zeros)
+    run([&](auto J) {
+        constexpr int ST = decltype(J)::value;
+        constexpr int PV = (ST + T::kStages - 2) % T::kStages;  // stage of step t-2
+        constexpr int NX = (ST + T::kStages - 1) % T::kStages;  // stage of step t-1
+        constexpr int NN = (ST + T::kAhead) % T::kStages;       // stage of step t+3
+        const uint32_t buf = pds + (ST % 2) * T::kPds;          // P/dS of step t-2
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    pb[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + ks * 64 * 16);
-                    db[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + (2 + ks) * 64 * 16);
-                }
-            cons.prefetch(ring, T::q_stage(PV));
-            wait_next();
-            fence_barrier();
-        },
-        [&](int, auto stage) {  // MFMA half: dV and dK of step i-1, loads of step i+kAhead-1
-            constexpr int ST = decltype(stage)::value, PV = (ST + T::kStages - 1) % T::kStages;
-            constexpr int NN = (ST + T::kAhead - 1) % T::kStages;
-            cons.template run<kDmaPerWave + 1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV),
-                                               [&](int k) { issue_k(iss, NN, k); });
-            advance(iss);
-            fence_barrier();
-        });
+            for (int ks = 0; ks < 2; ++ks) {
+                pb[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + ks * 64 * 16);
+                db[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + (2 + ks) * 64 * 16);
+            }
+        cons.template run<kDmaPerWave + 1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV),
+                                           [&](int k) { issue_k(iss, trow, srow, NN, k); });
+        advance_load(iss, trow, srow);
+        cons.prefetch(ring, T::q_stage(NX));
+        wait_next();
+        fence_barrier();
+    });
     // no load may still be writing this workgroup's LDS when it exits
     __builtin_amdgcn_s_waitcnt(0x70);
 
@@ -1155,7 +1199,8 @@ static hipError_t launch_pre(const void *o, const void *dout, const float *lse, 
     // Packed sequences lay lse and the statistics out as one sequence of
     // `total` tokens, so the pre-pass runs over all of them at once.
     const int64_t Bp = s.cu ? 1 : s.B, Np = s.cu ? s.total : s.N;
-    PreParams pp{o, dout, lse, stats, Np, s.o_rs, s.do_rs, (int32_t)Bp, s.Hq, s.d, bf16 ? 1 : 0};
+    PreParams pp{o, dout, lse, stats, Np, s.o_rs, s.do_rs, (int32_t)Bp, s.Hq, s.d, bf16 ? 1 : 0,
+                 s.scale};
     const int64_t rows = Bp * Np * s.Hq;
     const int lanes = s.d / (bf16 ? 8 : 4);  // lanes per row, as the kernel takes them
     const int64_t per_block = 256 / lanes;

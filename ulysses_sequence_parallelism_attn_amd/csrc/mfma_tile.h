@@ -280,6 +280,16 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
     return (const T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Lane L copies 16 bytes from gbase + voff to LDS at M0 + 16 L, with M0 set by
+// the compiler from `m0` (a wave-uniform LDS byte address); one wait state
+// separates the M0 write from the load.
+__device__ __forceinline__ void dma_b128_m0(const void *gbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma_b32_m0(const void *gbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "{m0}"(m0) : "memory");
+}
+
 // Lane L copies 16 (or 4) bytes from gbase + voff to LDS at ldst + 16 L (4 L).
 // gbase and ldst are wave-uniform; M0 (the LDS base of the transfer) is saved
 // and restored around the instruction.
