@@ -56,7 +56,9 @@ typedef enum {
     UL_ERR_ALIGNMENT = 5,    /* an attention tensor is not 16-byte aligned */
     UL_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ul_attn_bwd_workspace_bytes */
     UL_ERR_OVERLAP = 7,      /* an output's byte range overlaps an input or another output */
-    UL_ERR_HIP = 8           /* the HIP runtime reported an error at launch */
+    UL_ERR_HIP = 8,          /* the HIP runtime reported an error at launch */
+    UL_ERR_SCRATCH = 9       /* the problem needs more than the fixed scratch of
+                                ul_attn_bwd_noalloc (UL_NOALLOC_SCRATCH_BYTES) */
 } ul_status;
 
 typedef enum {
@@ -249,6 +251,34 @@ ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const 
                              int32_t n_seqs, int64_t total_tokens, int32_t max_seqlen, int32_t Hq,
                              int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
                              int32_t dtype, void *stream);
+
+/*
+ * ul_attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the caller passes inputs and outputs only, and the
+ * call allocates nothing.  The statistics that ul_attn_bwd keeps in its
+ * workspace go to a fixed array inside the library instead: a file-scope
+ * device array of UL_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held
+ * from the library's first use on that GPU until the process ends.  Its
+ * device address is looked up once per GPU (hipGetSymbolAddress, with that
+ * GPU current) on the first call there.
+ *
+ * Arguments, layouts, results and errors are those of ul_attn_bwd (results
+ * are bit-identical to it), except:
+ *   - SCRATCH when ul_attn_bwd_workspace_bytes(B, N, Hq, Hkv, head_dim, dtype)
+ *     exceeds UL_NOALLOC_SCRATCH_BYTES (for example B*Hq*N > 8M rows);
+ *   - HIP also when the array's address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's contents; each call writes all it reads before reading it.  Calls
+ * that may overlap in time on one GPU (two streams, two threads) race on the
+ * array: the caller must order them.
+ */
+#define UL_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+ul_status ul_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                              const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              float softmax_scale, int32_t causal, int32_t dtype, void *stream);
 
 /*
  * Sequence-sharded -> head-sharded relayout (the first all-to-all of the

@@ -33,6 +33,7 @@ def test_exports_every_declared_symbol(L):
     assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_fwd_varlen",
                           "ul_attn_bwd", "ul_attn_bwd_stages", "ul_attn_bwd_strided",
                           "ul_attn_bwd_varlen", "ul_attn_bwd_workspace_bytes",
+                          "ul_attn_bwd_noalloc",
                           "ul_relayout_s2h", "ul_relayout_h2s", "ul_relayout_s2h_heads",
                           "ul_relayout_h2s_heads", "ul_status_str"}
     for n in names:
@@ -274,3 +275,33 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
 def test_relayout_heads_validation(L, fn, args, code):
     a = [ctypes.c_void_p(args[0]), ctypes.c_void_p(args[1]), *args[2:], None]
     assert getattr(L, fn)(*a) == code
+
+
+def noalloc(L, **kw):
+    p = dict(Bsz=1, N=256, Hq=8, Hkv=2, d=128, scale=0.088, causal=1, dtype=B.UL_BF16)
+    p.update(kw)
+    ptrs = [kw.get(n, addr(i)) for i, n in enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk",
+                                                      "dv"])]
+    return L.ul_attn_bwd_noalloc(*ptrs, p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"], p["scale"],
+                                 p["causal"], p["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=ctypes.c_void_p(0)), 1), (dict(dv=ctypes.c_void_p(0)), 1),
+    (dict(N=0), 2), (dict(scale=0.0), 2), (dict(Hq=6, Hkv=4), 3), (dict(d=96), 4),
+    (dict(dq=ctypes.c_void_p(A + 8)), 5),
+    (dict(dk=ctypes.c_void_p(A + 64)), 7),            # dk overlaps q
+    (dict(N=1 << 21), 9), (dict(Bsz=3, N=1 << 20, Hq=4, Hkv=1), 9),  # beyond the fixed scratch
+])
+def test_noalloc_validation(L, kw, code):
+    """ul_attn_bwd_noalloc validates before touching the runtime; a problem whose statistics
+    exceed the fixed scratch is rejected with UL_ERR_SCRATCH."""
+    assert noalloc(L, **kw) == code
+
+
+def test_noalloc_scratch_limit_matches_workspace_size(L):
+    """The largest accepted problem is the one whose backward workspace fits the scratch."""
+    rows_max = B.NOALLOC_SCRATCH_BYTES // 8
+    assert L.ul_attn_bwd_workspace_bytes(1, rows_max // 4, 4, 1, 128, B.UL_BF16) <= B.NOALLOC_SCRATCH_BYTES
+    assert L.ul_attn_bwd_workspace_bytes(1, rows_max // 4 + 64, 4, 1, 128, B.UL_BF16) > B.NOALLOC_SCRATCH_BYTES
+    assert noalloc(L, N=rows_max // 4 + 64, Hq=4, Hkv=1) == 9

@@ -22,7 +22,8 @@ UL_F32, UL_BF16 = 0, 1
 UL_BWD_PREP, UL_BWD_DQ, UL_BWD_DKDV, UL_BWD_ALL = 1, 2, 4, 7
 STATUS = {0: "UL_OK", 1: "UL_ERR_NULL", 2: "UL_ERR_SHAPE", 3: "UL_ERR_DIVISIBILITY",
           4: "UL_ERR_UNSUPPORTED", 5: "UL_ERR_ALIGNMENT", 6: "UL_ERR_WORKSPACE",
-          7: "UL_ERR_OVERLAP", 8: "UL_ERR_HIP"}
+          7: "UL_ERR_OVERLAP", 8: "UL_ERR_HIP", 9: "UL_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.ul_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32,
                                   i32, f32, i32, i32, vp]
         L.ul_attn_bwd.restype = ctypes.c_int
+        L.ul_attn_bwd_noalloc.argtypes = [vp] * 9 + [i64, i64, i32, i32, i32, f32, i32, i32, vp]
+        L.ul_attn_bwd_noalloc.restype = ctypes.c_int
         L.ul_attn_bwd_stages.argtypes = [i32] + L.ul_attn_bwd.argtypes
         L.ul_attn_bwd_stages.restype = ctypes.c_int
         L.ul_attn_bwd_strided.argtypes = ([vp] * 10 + [sz, i64, i64, i32, i32, i32] + [i64] * 8 +
@@ -278,6 +281,33 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None,
     else:
         _check("ul_attn_fwd_strided", lib().ul_attn_fwd_strided(*head, *ts, *tail))
     return o, lse_t
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = True,
+                     dq=None, dk=None, dv=None, stream=None):
+    """attn_bwd through ul_attn_bwd_noalloc: no workspace argument, the library's fixed
+    per-GPU scratch holds the statistics (dense tensors only).  Calls that may overlap on
+    one GPU must be ordered by the caller."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4:
+        _fail("q and k must be 4-d [B, N, H, d]")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = torch.empty((B, N, Hq, d), dtype=q.dtype, device=q.device) if dq is None else dq
+    dk = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dk is None else dk
+    dv = torch.empty((B, N, Hkv, d), dtype=q.dtype, device=q.device) if dv is None else dv
+    check_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"),
+                 (dv, "dv")):
+        if not t.is_contiguous():
+            _fail(f"{n} must be contiguous")
+    st = lib().ul_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, N, Hq, Hkv, d, scale,
+                                   int(causal), _dtype_code(q), _stream(stream))
+    _check("ul_attn_bwd_noalloc", st)
+    return dq, dk, dv
 
 
 def _internal_workspace(nbytes: int, device, stream):

@@ -6,9 +6,48 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ul_internal.h"
 
+// Scratch of ul_attn_bwd_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// `scratch` itself to a kernel (its host-side name is not a device address):
+// the device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned char scratch[UL_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the null stream), looked up on the first call there
+// with that device current.
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 using ul::AttnShape;
 
@@ -165,6 +204,7 @@ const char *ul_status_str(ul_status s) {
         case UL_ERR_WORKSPACE: return "UL_ERR_WORKSPACE";
         case UL_ERR_OVERLAP: return "UL_ERR_OVERLAP";
         case UL_ERR_HIP: return "UL_ERR_HIP";
+        case UL_ERR_SCRATCH: return "UL_ERR_SCRATCH";
     }
     return "UL_ERR_UNKNOWN";
 }
@@ -264,7 +304,8 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
                    const void *dout, const float *lse, void *dq, void *dk, void *dv,
                    void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
                    int32_t Hkv, int32_t head_dim, const BwdStrides &ts, float softmax_scale,
-                   int32_t causal, int32_t dtype, void *stream, const Seqs *seqs) {
+                   int32_t causal, int32_t dtype, void *stream, const Seqs *seqs,
+                   bool use_scratch = false) {
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return UL_ERR_NULL;
     AttnSizes sz;
     ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
@@ -273,7 +314,14 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
     if (stages < 1 || (stages & ~UL_BWD_ALL) != 0) return UL_ERR_UNSUPPORTED;
     AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
     const size_t need = ul::attn_bwd_workspace_bytes(s, dtype);  // packed: B = 1, N = total
-    if (!workspace || workspace_bytes < need) return UL_ERR_WORKSPACE;
+    if (use_scratch) {
+        // the library's own array stands in for the workspace: it must hold the
+        // call, and it cannot overlap a caller's tensor
+        if (need > (size_t)UL_NOALLOC_SCRATCH_BYTES) return UL_ERR_SCRATCH;
+        workspace = nullptr;
+    } else if (!workspace || workspace_bytes < need) {
+        return UL_ERR_WORKSPACE;
+    }
     const int64_t es = elt_size(dtype), T = B * N;
     Rows r[8];
     if ((st = check_tensor(q, ts.q, T, Hq, head_dim, es, &r[0])) != UL_OK ||
@@ -289,11 +337,16 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
     const Rows ins[] = {r[0], r[1], r[2], r[3], r[4], dense(lse, sz.lse_bytes),
                         seqs ? dense(seqs->cu, ((int64_t)seqs->n + 1) * 4) : dense(nullptr, 0)};
     const Rows outs[] = {r[5], r[6], r[7], dense(workspace, (int64_t)need)};
-    for (int a = 0; a < 4; ++a) {
+    const int n_outs = use_scratch ? 3 : 4;
+    for (int a = 0; a < n_outs; ++a) {
         for (const Rows &in : ins)
             if (intersects(outs[a], in)) return UL_ERR_OVERLAP;
-        for (int c = a + 1; c < 4; ++c)
+        for (int c = a + 1; c < n_outs; ++c)
             if (intersects(outs[a], outs[c])) return UL_ERR_OVERLAP;
+    }
+    if (use_scratch) {  // every check above is done: only now touch the runtime
+        const hipError_t e = scratch_address(static_cast<hipStream_t>(stream), &workspace);
+        if (e != hipSuccess) return UL_ERR_HIP;
     }
     s.q_rs = ts.q;
     s.k_rs = ts.k;
@@ -433,6 +486,15 @@ ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const 
     return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, 1,
                     total_tokens, Hq, Hkv, head_dim, dense_strides(Hq, Hkv, head_dim),
                     softmax_scale, causal, dtype, stream, &sq);
+}
+
+ul_status ul_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                              const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                              int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
+                              float softmax_scale, int32_t causal, int32_t dtype, void *stream) {
+    return bwd_impl(UL_BWD_ALL, q, k, v, o, dout, lse, dq, dk, dv, nullptr, 0, B, N, Hq, Hkv,
+                    head_dim, dense_strides(Hq, Hkv, head_dim), softmax_scale, causal, dtype,
+                    stream, nullptr, true);
 }
 
 }  // extern "C"
