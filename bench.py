@@ -123,6 +123,58 @@ def ingest_pmc(fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
+N_XCD = 8          # GRBM_GUI_ACTIVE is summed over the XCDs; one XCD's count is the clock
+N_SIMD = 256 * 4   # SQ_VALU_MFMA_BUSY_CYCLES is summed over every SIMD
+
+
+def summarize_pmc(dirs: list) -> str:
+    """Per-kernel counters of rocprofv3 --pmc runs (last dispatch of each kernel) as a markdown
+    table, with the derived MFMA utilisation (busy cycles over one XCD's active cycles times
+    the SIMD count), shader clock and MFMA rate."""
+    import csv
+
+    vals: dict = {}
+    ms: dict = {}
+    for d in dirs:
+        f = next(Path(d).rglob("*counter_collection.csv"))
+        for r in sorted(csv.DictReader(open(f)), key=lambda r: int(r["Dispatch_Id"])):
+            key = next((short for pat, short in KERNEL_NAMES if pat in r["Kernel_Name"]), None)
+            if key is None:
+                continue
+            vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            ms.setdefault(key, {})[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+    lines = ["| kernel | ms | clock (GHz) | MFMA busy | MFMA TFLOP/s | VALU instr / MFMA | LDS instr / MFMA "
+             "| LDS bank conflicts / LDS active cycles | MFMA-VALU co-issue cycles / MFMA busy |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for _, key in KERNEL_NAMES:
+        if key not in vals:
+            continue
+        v = vals[key]
+        t = sum(ms[key].values()) / len(ms[key])
+        gui = v.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        n_mfma = mops * 512 / (2 * 32 * 32 * 16)
+        cell = lambda x: f"{x:.3g}" if x is not None else "-"
+        util = busy / (gui * N_SIMD) if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in v else None
+        valu = (v["SQ_INSTS_VALU"] - n_mfma) / n_mfma if n_mfma and "SQ_INSTS_VALU" in v else None
+        lds = v["SQ_INSTS_LDS"] / n_mfma if n_mfma and "SQ_INSTS_LDS" in v else None
+        bank = (v["SQ_LDS_BANK_CONFLICT"] / v["SQ_LDS_IDX_ACTIVE"]
+                if v.get("SQ_LDS_IDX_ACTIVE") else None)
+        coex = v["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy if busy and "SQ_VALU_MFMA_COEXEC_CYCLES" in v else None
+        lines.append(f"| {key} | {t:.3f} | {cell(gui / (t * 1e-3) / 1e9 if gui else None)} | "
+                     f"{cell(util)} | {cell(mops * 512 / (t * 1e-3) / 1e12 if mops else None)} | "
+                     f"{cell(valu)} | {cell(lds)} | {cell(bank)} | {cell(coex)} |")
+    raw = ["", "Raw counters (last dispatch of each kernel):", ""]
+    names = sorted({c for v in vals.values() for c in v})
+    raw.append("| kernel | " + " | ".join(names) + " |")
+    raw.append("|---|" + "---|" * len(names))
+    for _, key in KERNEL_NAMES:
+        if key in vals:
+            raw.append(f"| {key} | " + " | ".join(f"{vals[key].get(c, float('nan')):.4g}" for c in names) + " |")
+    return "\n".join(lines + raw)
+
+
 def cpu_model() -> str:
     """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
     import subprocess
@@ -376,10 +428,17 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy first (a known-size reference for "
                          "HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="PMC_DIR",
+                    help="print a markdown table of the attention kernels' counters from rocprofv3 "
+                         "--pmc output folders and exit")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc output folders "
                          "(FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration) and exit")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return 0
 
     if args.ingest_pmc:
         rec = ingest_pmc(*args.ingest_pmc)
