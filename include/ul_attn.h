@@ -258,7 +258,7 @@ ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const 
  * that forbid hipMalloc): the caller passes inputs and outputs only, and the
  * call allocates nothing.  The statistics that ul_attn_bwd keeps in its
  * workspace go to a fixed array inside the library instead: a file-scope
- * device array of UL_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, held
+ * device array of UL_NOALLOC_SCRATCH_BYTES (256 MiB), one copy per GPU, held
  * from the library's first use on that GPU until the process ends.  Its
  * device address is looked up once per GPU (hipGetSymbolAddress, with that
  * GPU current) on the first call there.
@@ -266,14 +266,16 @@ ul_status ul_attn_bwd_varlen(const void *q, const void *k, const void *v, const 
  * Arguments, layouts, results and errors are those of ul_attn_bwd (results
  * are bit-identical to it), except:
  *   - SCRATCH when ul_attn_bwd_workspace_bytes(B, N, Hq, Hkv, head_dim, dtype)
- *     exceeds UL_NOALLOC_SCRATCH_BYTES (for example B*Hq*N > 8M rows);
+ *     exceeds UL_NOALLOC_SCRATCH_BYTES (8 bytes per query row and head, plus
+ *     the head-split partials of shorter sequences: B*Hq*N beyond about 32M
+ *     rows, or less for the shorter sequences that use the partials);
  *   - HIP also when the array's address cannot be obtained.
  * Every call on one GPU uses that GPU's one array, which keeps the last
  * call's contents; each call writes all it reads before reading it.  Calls
  * that may overlap in time on one GPU (two streams, two threads) race on the
  * array: the caller must order them.
  */
-#define UL_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define UL_NOALLOC_SCRATCH_BYTES (256u << 20)
 
 ul_status ul_attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
                               const void *dout, const float *lse, void *dq, void *dk, void *dv,

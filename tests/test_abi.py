@@ -291,7 +291,7 @@ def noalloc(L, **kw):
     (dict(N=0), 2), (dict(scale=0.0), 2), (dict(Hq=6, Hkv=4), 3), (dict(d=96), 4),
     (dict(dq=ctypes.c_void_p(A + 8)), 5),
     (dict(dk=ctypes.c_void_p(A + 64)), 7),            # dk overlaps q
-    (dict(N=1 << 21), 9), (dict(Bsz=3, N=1 << 20, Hq=4, Hkv=1), 9),  # beyond the fixed scratch
+    (dict(N=1 << 23), 9), (dict(Bsz=9, N=1 << 20, Hq=4, Hkv=1), 9),  # beyond the fixed scratch
 ])
 def test_noalloc_validation(L, kw, code):
     """ul_attn_bwd_noalloc validates before touching the runtime; a problem whose statistics

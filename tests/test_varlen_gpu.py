@@ -94,7 +94,11 @@ def test_varlen_full_parity(dtype, lengths, Hq, Hkv, d, causal):
 
 
 def test_varlen_metric_size_matches_per_sequence_calls():
-    """65536 packed tokens of the seeded length mix equal the plain call on each sequence."""
+    """65536 packed tokens of the seeded length mix equal the plain call on each sequence:
+    O, lse and dQ bit for bit.  dK and dV to 1e-3 relative L2: a plain call on a sequence
+    this short runs its longest key blocks one query head at a time and sums the heads'
+    fp32 partials afterwards, a different summation order from the packed call's (which the
+    float64 oracle checks on its own in test_varlen_full_parity)."""
     B = _B()
     lengths = synth.length_mix(65536, seed=3008)
     cu = synth.cu_seqlens(lengths)
@@ -116,9 +120,12 @@ def test_varlen_metric_size_matches_per_sequence_calls():
         o1, l1 = B.attn_fwd(sl(q), sl(k), sl(v), scale, True)
         dq1, dk1, dv1 = B.attn_bwd(sl(q), sl(k), sl(v), o1, sl(do), l1, scale, True)
         torch.cuda.synchronize()
-        for name, x, r in (("o", o[a:b], o1[0]), ("dq", dq[a:b], dq1[0]), ("dk", dk[a:b], dk1[0]),
-                           ("dv", dv[a:b], dv1[0]), ("lse", lse[:, a:b], l1[0])):
+        for name, x, r in (("o", o[a:b], o1[0]), ("dq", dq[a:b], dq1[0]), ("lse", lse[:, a:b], l1[0])):
             assert torch.equal(_bits(x.contiguous()), _bits(r.contiguous())), f"seq {s} {name}"
+        for name, x, r in (("dk", dk[a:b], dk1[0]), ("dv", dv[a:b], dv1[0])):
+            x32, r32 = x.float(), r.float()
+            rel = float((x32 - r32).norm() / r32.norm())
+            assert rel <= 1e-3, f"seq {s} {name}: rel-L2 {rel:.3g} against the plain call"
 
 
 def test_varlen_uncovered_tokens_stay_unwritten():

@@ -59,8 +59,8 @@ def test_noalloc_rejects_problems_beyond_the_scratch():
     """A problem whose statistics exceed the fixed scratch raises UL_ERR_SCRATCH and
     leaves the outputs untouched (checked on the host before any launch)."""
     B = _B()
-    # B*Hq*N = 8M + 64 rows of statistics, past the 64 MiB scratch; tiny head_dim 64 tensors
-    Bsz, N, Hq, Hkv, d = 1, (1 << 21) + 16, 4, 1, 64
+    # B*Hq*N = 32M + 64 rows of statistics, past the 256 MiB scratch; head_dim 64 tensors
+    Bsz, N, Hq, Hkv, d = 1, (1 << 23) + 16, 4, 1, 64
     q = torch.zeros((Bsz, N, Hq, d), dtype=torch.bfloat16, device="cuda")
     k = torch.zeros((Bsz, N, Hkv, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((Bsz, Hq, N), dtype=torch.float32, device="cuda")

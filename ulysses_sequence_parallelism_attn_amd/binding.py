@@ -23,7 +23,7 @@ UL_BWD_PREP, UL_BWD_DQ, UL_BWD_DKDV, UL_BWD_ALL = 1, 2, 4, 7
 STATUS = {0: "UL_OK", 1: "UL_ERR_NULL", 2: "UL_ERR_SHAPE", 3: "UL_ERR_DIVISIBILITY",
           4: "UL_ERR_UNSUPPORTED", 5: "UL_ERR_ALIGNMENT", 6: "UL_ERR_WORKSPACE",
           7: "UL_ERR_OVERLAP", 8: "UL_ERR_HIP", 9: "UL_ERR_SCRATCH"}
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 _lib = None
 

@@ -28,6 +28,7 @@
 // are rounded to bf16 for the MFMA.  fp32 kernels are plain VALU loops (the
 // exactness path).
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -500,6 +501,12 @@ struct DkvParams {
     int32_t n_kblk;
     float scale_log2, scale;
     int32_t causal;
+    // Head-split key blocks (shorter sequences): blocks 0 .. ksplit-1 run as
+    // one workgroup per query head of the group, each writing its fp32 partial
+    // dK (unscaled) and dV to part_k / part_v [ksplit][B][Hkv][grp][128][D];
+    // a reduction kernel sums the heads.  0: every block is one workgroup.
+    int32_t ksplit;
+    float *part_k, *part_v;
 };
 
 // LDS: the Q tiles of every stage, then the dO tiles, the statistics rows and
@@ -686,12 +693,28 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     const bool producer = wave < kKvPairs;
     const int pair = producer ? wave : wave - kKvPairs;
 
-    // item = kblk * (B*Hkv) + (b*Hkv + g): key block 0 (the most work) first
+    // Items: first the head-split blocks, ((kblk * B + b) * Hkv + g) * grp +
+    // head, then the whole blocks, kblk * (B*Hkv) + (b*Hkv + g), each part
+    // with key block 0 (the most work) first.
     const int per_rank = p.B * p.Hkv;
-    const int kblk = item / per_rank;
-    const int bg = item - kblk * per_rank;
-    const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int grp = p.Hq / p.Hkv;
+    const int n_split = p.ksplit * per_rank * grp;
+    int kblk, bg, hsel;
+    if (item < n_split) {
+        kblk = item / (per_rank * grp);
+        const int rest = item - kblk * per_rank * grp;
+        bg = rest / grp;
+        hsel = rest - bg * grp;
+    } else {
+        const int it = item - n_split;
+        kblk = p.ksplit + it / per_rank;
+        bg = it - (kblk - p.ksplit) * per_rank;
+        hsel = -1;
+    }
+    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    const bool split = hsel >= 0;
+    const int gsteps = split ? 1 : grp;  // query heads this workgroup walks
+    const int h0 = split ? hsel : 0;     // the first of them within the group
     const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
     const int N = sq.len;
     const int kb0 = kblk * kKeysPerWg;
@@ -706,14 +729,14 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     const int qt_first = p.causal ? kb0 / kQT : 0;
     const int nqt = (N + kQT - 1) / kQT;
     const int per_head = nqt - qt_first;
-    const int nsteps = per_head * grp;
+    const int nsteps = per_head * gsteps;
     struct Cur {
         int s, hi, r0;
     };
     auto advance = [&](Cur &cu) {  // stays on the last step once there
         if (cu.s + 1 < nsteps) {
             ++cu.s;
-            if (++cu.hi == grp) {
+            if (++cu.hi == gsteps) {
                 cu.hi = 0;
                 cu.r0 -= kQT;
             }
@@ -785,7 +808,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         // drops by a tile every grp steps.
         const int mlo = kb0 + kKeysPerWg > N ? INT_MAX : (p.causal ? kb0 + kKeysPerWg : INT_MIN);
         const int mhi = N - kQT;
-        int r0 = first.r0, hc = grp, left = nsteps;
+        int r0 = first.r0, hc = gsteps, left = nsteps;
         auto prepare = [&](f32x16 &sinit) {  // mask the S starting values of the step at (r0, left)
             if (left <= 0 || r0 < mlo || r0 > mhi) {
                 if (left <= 0) {
@@ -799,7 +822,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         auto next_step = [&]() {
             --left;
             if (--hc == 0) {
-                hc = grp;
+                hc = gsteps;
                 r0 -= kQT;
             }
         };
@@ -909,8 +932,8 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             wait_vm_only<kDmaPerWave>();
     };
     // The cursor of the step to load next, with its row pointers.
-    const uint16_t *trow0 = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)g * grp * D;
-    const float *srow0 = p.stats + sq.st0 + (int64_t)g * grp * head_stride_st + first.r0;
+    const uint16_t *trow0 = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)(g * grp + h0) * D;
+    const float *srow0 = p.stats + sq.st0 + (int64_t)(g * grp + h0) * head_stride_st + first.r0;
     const int64_t trow_step = (int64_t)kQT * t_rs;
     auto advance_load = [&](Cur &cu, const uint16_t *&trow, const float *&srow) {
         const int r0 = cu.r0;
@@ -981,6 +1004,30 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // no load may still be writing this workgroup's LDS when it exits
     __builtin_amdgcn_s_waitcnt(0x70);
 
+    if (split) {  // fp32 partials of this head; the reduction scales and rounds
+        const int64_t blk = (((int64_t)kblk * p.B + b) * p.Hkv + g) * grp + hsel;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int kl = (2 * kh + k2) * kKeysPerWave + m;  // key within the block
+            float *pk = p.part_k + (blk * kKeysPerWg + kl) * D;
+            float *pv = p.part_v + (blk * kKeysPerWg + kl) * D;
+#pragma unroll
+            for (int e2 = 0; e2 < EBC; ++e2)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int e = (eh * EBC + e2) * 32 + r4 * 8 + kg * 4;
+                    f32x4 k4, v4;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        k4[q] = dkacc[e2][k2][r4 * 4 + q];
+                        v4[q] = dvacc[e2][k2][r4 * 4 + q];
+                    }
+                    *reinterpret_cast<f32x4 *>(pk + e) = k4;
+                    *reinterpret_cast<f32x4 *>(pv + e) = v4;
+                }
+        }
+        return;
+    }
     // dK = scale * acc, dV = acc (bf16): lane column = key, registers = head dim
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -1011,11 +1058,54 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dkdv_bf16_kernel(DkvParam
     dkdv_body<D>(p, blockIdx.x);
 }
 
+// Sum of the head-split partials: for key j of a split block, dK = scale *
+// sum over the group's query heads of part_k, dV = sum of part_v, rounded to
+// bf16.  One thread per 4 head dims of one key, heads summed in order.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkvParams p) {
+    const int grp = p.Hq / p.Hkv;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.ksplit * p.B * p.Hkv * kKeysPerWg * (D / 4);
+    if (idx >= total) return;
+    const int d4 = (int)(idx % (D / 4));
+    int64_t r = idx / (D / 4);
+    const int kl = (int)(r % kKeysPerWg);
+    r /= kKeysPerWg;
+    const int g = (int)(r % p.Hkv);
+    r /= p.Hkv;
+    const int b = (int)(r % p.B);
+    const int kblk = (int)(r / p.B);
+    const int key = kblk * kKeysPerWg + kl;
+    if (key >= p.N) return;
+    const int64_t blk0 = (((int64_t)kblk * p.B + b) * p.Hkv + g) * grp;
+    f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < grp; ++h) {
+        const int64_t off = ((blk0 + h) * kKeysPerWg + kl) * D + d4 * 4;
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p.part_k + off);
+        const f32x4 c = *reinterpret_cast<const f32x4 *>(p.part_v + off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sk[q] += a[q];
+            sv[q] += c[q];
+        }
+    }
+    bf16x4 k4, v4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        k4[q] = (__bf16)(sk[q] * p.scale);
+        v4[q] = (__bf16)sv[q];
+    }
+    const int64_t tok = (int64_t)b * p.N + key;
+    *reinterpret_cast<u32x2 *>(p.dk + tok * p.dk_rs + (int64_t)g * D + d4 * 4) = __builtin_bit_cast(u32x2, k4);
+    *reinterpret_cast<u32x2 *>(p.dv + tok * p.dv_rs + (int64_t)g * D + d4 * 4) = __builtin_bit_cast(u32x2, v4);
+}
+
 // Both backward passes in one launch, for grids too small to fill the chip
 // on their own (short sequences): the dK/dV work items (the longer ones)
 // first, then the dQ items, so the two passes share the compute units instead
 // of each leaving part of them idle.  Each workgroup runs exactly the body of
-// the standalone kernel for its item.
+// the standalone kernel for its item.  (Interleaving the two families in
+// proportion to their counts measured 2-4 % slower at N = 8192 and 16384.)
 static_assert(kQThreads == kKvThreads, "one block size for both passes");
 template <int D>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_dkdv_bf16_kernel(DqParams dp, DkvParams kp,
@@ -1187,11 +1277,48 @@ __global__ __launch_bounds__(kF32KvKeys) void attn_bwd_dkdv_f32_kernel(BwdF32Par
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Head-split dK/dV for shorter sequences.  When the dK/dV grid is at most
+// half a round of the 256 compute units, the longest work item (key block 0:
+// every query row of every head of the group) is far longer than the average
+// work per compute unit, and it alone sets the backward's time.  Key blocks
+// whose whole item would exceed the longest single-head item then run as one
+// workgroup per query head (fp32 partials, summed by dkdv_reduce_kernel).
+// Measured (8q/2kv, d = 128, whole backward): N = 4096 0.37 -> 0.19 ms, 8192
+// 0.76 -> 0.54 ms; at 16384 (256 items) neutral, so the split stops there.
+// The plan depends on the sizes only (not on the mask or the device), so the
+// workspace size does too.
+constexpr int64_t kSplitMaxItems = 128;
+constexpr size_t kSplitMaxBytes = size_t(192) << 20;
+
+struct BwdPlan {
+    int32_t ksplit;       // key blocks run head by head
+    size_t stats_bytes;   // -lse/scale and -D per query row and head
+    size_t part_bytes;    // fp32 partials of dK and dV of the split blocks
+};
+
+BwdPlan bwd_plan(const AttnShape &s, int32_t dtype) {
+    BwdPlan pl{0, 0, 0};
+    const size_t rows = s.cu ? (size_t)s.Hq * (size_t)s.total : (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
+    pl.stats_bytes = round256(2 * rows * sizeof(float));
+    const int64_t grp = s.Hq / s.Hkv;
+    const int64_t n_kblk = (s.N + kKeysPerWg - 1) / kKeysPerWg;
+    if (dtype != UL_BF16 || s.cu || grp < 2 || n_kblk * s.B * s.Hkv > kSplitMaxItems) return pl;
+    const int64_t nqt = (s.N + kQT - 1) / kQT;
+    int64_t ks = 0;
+    // the causal rule for both masks: the workspace size takes no mask argument
+    while (ks < n_kblk && grp * (nqt - ks * (kKeysPerWg / kQT)) > nqt) ++ks;
+    const size_t per_block = (size_t)s.B * s.Hkv * grp * kKeysPerWg * s.d * sizeof(float) * 2;
+    ks = std::min<int64_t>(ks, (int64_t)(kSplitMaxBytes / per_block));
+    pl.ksplit = (int32_t)ks;
+    pl.part_bytes = (size_t)ks * per_block;
+    return pl;
+}
+
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t /*dtype*/) {
-    const size_t rows = s.cu ? (size_t)s.Hq * (size_t)s.total : (size_t)s.B * (size_t)s.Hq * (size_t)s.N;
-    return round256(2 * rows * sizeof(float));
+size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t dtype) {
+    const BwdPlan pl = bwd_plan(s, dtype);
+    return pl.stats_bytes + pl.part_bytes;
 }
 
 static hipError_t launch_pre(const void *o, const void *dout, const float *lse, float *stats,
@@ -1282,8 +1409,23 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
     kp.scale_log2 = dp.scale_log2;
     kp.scale = s.scale;
     kp.causal = s.causal;
-    const int64_t kv_items = (int64_t)kp.n_kblk * kp.B * kp.Hkv;
+    const BwdPlan plan = bwd_plan(s, UL_BF16);
+    kp.ksplit = plan.ksplit;
+    kp.part_k = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + plan.stats_bytes);
+    kp.part_v = kp.part_k + plan.part_bytes / sizeof(float) / 2;
+    const int64_t kv_items = (int64_t)kp.n_kblk * kp.B * kp.Hkv + (int64_t)plan.ksplit * kp.B * kp.Hkv * (grp - 1);
     if (kv_items > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // the reduction of the head-split partials, after the dK/dV work items
+    auto reduce = [&]() -> hipError_t {
+        if (plan.ksplit == 0) return hipSuccess;
+        const int64_t n = (int64_t)plan.ksplit * kp.B * kp.Hkv * kKeysPerWg * (s.d / 4);
+        const dim3 grid((uint32_t)((n + 255) / 256)), block(256);
+        if (s.d == 128)
+            hipLaunchKernelGGL(dkdv_reduce_kernel<128>, grid, block, 0, stream, kp);
+        else
+            hipLaunchKernelGGL(dkdv_reduce_kernel<64>, grid, block, 0, stream, kp);
+        return hipGetLastError();
+    };
 
     // Shorter sequences: when the dK/dV grid covers fewer than four rounds of
     // the compute units, run both passes in one launch so they fill the chip
@@ -1295,7 +1437,7 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
         if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
         if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
             return err;
-        if (kv_items < 4 * (int64_t)cus) {
+        if ((int64_t)kp.n_kblk * kp.B * kp.Hkv < 4 * (int64_t)cus) {
             const dim3 grid((uint32_t)(kv_items + dq_items)), block(kKvThreads);
             if (s.d == 128) {
                 constexpr size_t lds = DqTile<128>::kLds > DkvTile<128>::kLds ? DqTile<128>::kLds
@@ -1310,7 +1452,8 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
                 hipLaunchKernelGGL(attn_bwd_dq_dkdv_bf16_kernel<64>, grid, block, lds, stream, dp, kp,
                                    (int)kv_items);
             }
-            return hipGetLastError();
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            return reduce();
         }
     }
 
@@ -1325,6 +1468,8 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
             if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<128>, DkvTile<128>::kLds)) != hipSuccess) return err;
             hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<128>, dim3((uint32_t)kv_items), dim3(kKvThreads),
                                DkvTile<128>::kLds, stream, kp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            if ((err = reduce()) != hipSuccess) return err;
         }
     } else {
         if (stages & UL_BWD_DQ) {
@@ -1337,6 +1482,8 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
             if ((err = allow_lds(attn_bwd_dkdv_bf16_kernel<64>, DkvTile<64>::kLds)) != hipSuccess) return err;
             hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, dim3((uint32_t)kv_items), dim3(kKvThreads),
                                DkvTile<64>::kLds, stream, kp);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            if ((err = reduce()) != hipSuccess) return err;
         }
     }
     return hipGetLastError();
