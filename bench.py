@@ -56,13 +56,14 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str) -> float | None:
-    """HBM bytes per launch from the committed PMC measurement, if the kernels are unchanged."""
+def measured_traffic(kernel: str, workload: str) -> float | None:
+    """HBM bytes per launch from the committed PMC measurement, if it was taken on this
+    workload and the kernels are unchanged."""
     try:
         rec = json.loads(TRAFFIC_FILE.read_text())
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_hash") != kernel_hash():
+    if rec.get("kernel_hash") != kernel_hash() or rec.get("workload") != workload:
         return None
     v = rec.get("bytes_per_launch", {}).get(kernel)
     return float(v) if v is not None else None
@@ -102,14 +103,14 @@ def _pmc_per_kernel(csv_path: Path, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def ingest_pmc(fetch_dir: str, write_dir: str) -> dict:
+def ingest_pmc(fetch_dir: str, write_dir: str, workload: str) -> dict:
     """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch),
     each scaled by what the same counter reads for the 1 GiB calibration copy."""
     fetch = _pmc_per_kernel(next(Path(fetch_dir).rglob("*counter_collection.csv")), "FETCH_SIZE")
     write = _pmc_per_kernel(next(Path(write_dir).rglob("*counter_collection.csv")), "WRITE_SIZE")
     f_cal = CALIBRATION_BYTES / (fetch[CALIBRATION_KERNEL] * 1024.0)
     w_cal = CALIBRATION_BYTES / (write[CALIBRATION_KERNEL] * 1024.0)
-    rec = {"kernel_hash": kernel_hash(),
+    rec = {"kernel_hash": kernel_hash(), "workload": workload,
            "calibration": {"kernel": CALIBRATION_KERNEL, "bytes": CALIBRATION_BYTES,
                            "fetch_kib": fetch[CALIBRATION_KERNEL], "write_kib": write[CALIBRATION_KERNEL],
                            "fetch_factor": f_cal, "write_factor": w_cal},
@@ -441,7 +442,9 @@ def main() -> int:
         return 0
 
     if args.ingest_pmc:
-        rec = ingest_pmc(*args.ingest_pmc)
+        from ulysses_sequence_parallelism_attn_amd import synth
+
+        rec = ingest_pmc(*args.ingest_pmc, synth.WORKLOADS[args.workload].name)
         TRAFFIC_FILE.parent.mkdir(exist_ok=True)
         TRAFFIC_FILE.write_text(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec["bytes_per_launch"]))
@@ -479,6 +482,9 @@ def main() -> int:
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(B.workspace_bytes(wl.B, wl.N, wl.Hq, wl.Hkv, wl.d, B.UL_BF16),
                      dtype=torch.uint8, device=dev)
+    # the forward's key-range split takes a workspace at shorter N (none at N = 65536)
+    fws_bytes = B.fwd_workspace_bytes(wl.B, wl.N, wl.Hq, wl.Hkv, wl.d, B.UL_BF16)
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev) if fws_bytes else None
     stream = torch.cuda.current_stream()
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -489,24 +495,33 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # One step: relayout s2h, forward, the backward's three stages, relayout h2s.  The
-    # backward runs as its three C-ABI stages (exactly what ul_attn_bwd launches) so that
-    # each kernel is bracketed by its own events on the stream it is launched on.
-    names = ["relayout_s2h", "attn_fwd", "attn_bwd_prep", "attn_bwd_dq", "attn_bwd_dkdv",
-             "relayout_h2s"]
+    # One step: relayout s2h, forward, the backward's stages, relayout h2s.  The backward
+    # runs as C-ABI stage calls that launch exactly what ul_attn_bwd launches, so that each
+    # kernel is bracketed by its own events on the stream it is launched on: PREP, then DQ
+    # and DKDV as separate calls where ul_attn_bwd launches them separately, or as one DQ|DKDV
+    # call where it merges them into one launch (its rule: fewer 128-key dK/dV blocks than
+    # four per compute unit).
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    merged_bwd = -(-wl.N // 128) * wl.B * wl.Hkv < 4 * cus
 
     def bwd_stage(stage):
         return lambda: B.attn_bwd(q, k, v, o, do, lse, wl.scale, True, workspace=ws, dq=dq, dk=dk,
                                   dv=dv, stages=stage)
 
+    names = ["relayout_s2h", "attn_fwd", "attn_bwd_prep"]
     calls = [
         lambda: B.relayout_s2h(x, P, out=y),
-        lambda: B.attn_fwd(q, k, v, wl.scale, True, out=o, lse=lse),
+        lambda: B.attn_fwd(q, k, v, wl.scale, True, out=o, lse=lse, workspace=fws),
         bwd_stage(B.UL_BWD_PREP),
-        bwd_stage(B.UL_BWD_DQ),
-        bwd_stage(B.UL_BWD_DKDV),
-        lambda: B.relayout_h2s(y, out=x2),
     ]
+    if merged_bwd:
+        names += ["attn_bwd_dq_dkdv"]
+        calls += [bwd_stage(B.UL_BWD_DQ | B.UL_BWD_DKDV)]
+    else:
+        names += ["attn_bwd_dq", "attn_bwd_dkdv"]
+        calls += [bwd_stage(B.UL_BWD_DQ), bwd_stage(B.UL_BWD_DKDV)]
+    names += ["relayout_h2s"]
+    calls += [lambda: B.relayout_h2s(y, out=x2)]
 
     def step(ev=None):
         for j, call in enumerate(calls):
@@ -565,22 +580,27 @@ def main() -> int:
         "relayout_s2h": hbm(rl_bytes, "relayout_s2h"),
         "attn_fwd": mfma(f_fwd, "attn_fwd"),
         "attn_bwd_prep": hbm(prep_bytes, "attn_bwd_prep"),
+    }
+    if merged_bwd:
+        # one launch does both passes: 10d per pair counted, 14d performed
+        roof["attn_bwd_dq_dkdv"] = mfma(10.0 * wl.d * pairs_x_heads, "attn_bwd_dq_dkdv",
+                                        14.0 * wl.d * pairs_x_heads)
+    else:
         # the method counts the dQ pass only for its dQ contraction (2d per pair; S and dP
         # are counted once, in dK/dV); it performs S, dP and dQ (6d per pair)
-        "attn_bwd_dq": mfma(2.0 * wl.d * pairs_x_heads, "attn_bwd_dq", 6.0 * wl.d * pairs_x_heads),
-        "attn_bwd_dkdv": mfma(8.0 * wl.d * pairs_x_heads, "attn_bwd_dkdv"),
-        "relayout_h2s": hbm(rl_bytes, "relayout_h2s"),
-    }
+        roof["attn_bwd_dq"] = mfma(2.0 * wl.d * pairs_x_heads, "attn_bwd_dq", 6.0 * wl.d * pairs_x_heads)
+        roof["attn_bwd_dkdv"] = mfma(8.0 * wl.d * pairs_x_heads, "attn_bwd_dkdv")
+    roof["relayout_h2s"] = hbm(rl_bytes, "relayout_h2s")
     for n, r in roof.items():
         r["frac"] = r["achieved"] / r["peak"]
         r["ms"] = avg[n]
-        r["traffic"] = measured_traffic(n)
+        r["traffic"] = measured_traffic(n, wl.name)
     dominant = max(avg, key=avg.get)
     dom = {k2: roof[dominant][k2] for k2 in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     dom["kernel"] = dominant
     dom["ms"] = avg[dominant]
 
-    attn_ms = avg["attn_fwd"] + avg["attn_bwd_prep"] + avg["attn_bwd_dq"] + avg["attn_bwd_dkdv"]
+    attn_ms = sum(t for n, t in avg.items() if n.startswith("attn_"))
     out = {
         "metric": METRIC,
         "value": value,
@@ -604,6 +624,8 @@ def main() -> int:
         "roofline": dom,
         "roofline_all": roof,
         "kernel_hash": kernel_hash(),
+        "bwd_launch": "dq+dkdv merged" if merged_bwd else "dq, dkdv separate",
+        "fwd_split": bool(fws_bytes),
     }
     if not args.no_copy_ceiling:
         out["copy_ceiling"] = copy_ceiling(torch, x)

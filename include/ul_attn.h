@@ -15,6 +15,8 @@
  *   ul_attn_fwd       causal (or full) softmax attention over the full N for a
  *                     slice of query heads with grouped KV heads, also
  *                     returning the per-row logsumexp;
+ *   ul_attn_fwd_ws    the same with a workspace, which lets shorter causal
+ *                     sequences split the key range of their longest rows;
  *   ul_attn_bwd       its gradient (dQ, dK, dV);
  *   ul_attn_*_strided the same on token-strided views, so that a rank's head
  *                     slice is read from and written to sequence-sharded
@@ -54,7 +56,7 @@ typedef enum {
     UL_ERR_DIVISIBILITY = 3, /* Hq % Hkv, H % P or N % P is non-zero, or P < 1 */
     UL_ERR_UNSUPPORTED = 4,  /* head_dim or dtype outside what the kernels implement */
     UL_ERR_ALIGNMENT = 5,    /* an attention tensor is not 16-byte aligned */
-    UL_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ul_attn_bwd_workspace_bytes */
+    UL_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than ul_attn_*_workspace_bytes */
     UL_ERR_OVERLAP = 7,      /* an output's byte range overlaps an input or another output */
     UL_ERR_HIP = 8,          /* the HIP runtime reported an error at launch */
     UL_ERR_SCRATCH = 9       /* the problem needs more than the fixed scratch of
@@ -94,6 +96,41 @@ typedef enum {
 ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                       int64_t B, int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim,
                       float softmax_scale, int32_t causal, int32_t dtype, void *stream);
+
+/*
+ * Device workspace bytes that ul_attn_fwd_ws needs for these sizes (causal
+ * assumed; a multiple of 16).  0 where the sizes run the key range unsplit:
+ * the fp32 dtype, and bf16 calls with too many work items for the split to
+ * pay (B x Hkv x query blocks above 256, the CU count of the part) or too few
+ * query blocks (N of a few hundred).  At most 34 MB.  0 for invalid sizes.
+ */
+size_t ul_attn_fwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t dtype);
+
+/*
+ * ul_attn_fwd with a workspace.  Same result definition, layouts and
+ * determinism; on bf16 causal calls where ul_attn_fwd_workspace_bytes is
+ * non-zero, the upper half of the query blocks is computed as two halves of
+ * its key range whose partial softmax sums (running max m, sum l and the
+ * unnormalised output, fp32) are combined afterwards by the same rescaling
+ * that the online softmax applies between key tiles ("Why Train Million-Token
+ * Contexts Anyway?": attention over long N is computed in tiles of keys, the
+ * softmax kept in running form).  The result differs from ul_attn_fwd only in
+ * rounding: the order of the fp32 sums changes for those rows.  Whether a
+ * call splits depends on its sizes (B, N, Hq, Hkv), so the same head may
+ * round differently in calls of different sizes; a given call is
+ * deterministic.
+ *   workspace        device buffer of at least ul_attn_fwd_workspace_bytes(
+ *                    B, N, Hq, Hkv, head_dim, dtype) bytes, 16-byte aligned;
+ *                    may be NULL when that is 0.  Its contents on entry are
+ *                    ignored and on return unspecified.
+ * Errors: as ul_attn_fwd, plus WORKSPACE, and OVERLAP when the workspace
+ * overlaps an input or an output.
+ */
+ul_status ul_attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                         void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
+                         int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                         int32_t dtype, void *stream);
 
 /*
  * ul_attn_fwd on token-strided tensors: the head slice of one rank read from,

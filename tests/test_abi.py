@@ -31,6 +31,7 @@ def addr(i):
 def test_exports_every_declared_symbol(L):
     names = B.declared_functions()
     assert set(names) == {"ul_attn_fwd", "ul_attn_fwd_strided", "ul_attn_fwd_varlen",
+                          "ul_attn_fwd_ws", "ul_attn_fwd_workspace_bytes",
                           "ul_attn_bwd", "ul_attn_bwd_stages", "ul_attn_bwd_strided",
                           "ul_attn_bwd_varlen", "ul_attn_bwd_workspace_bytes",
                           "ul_attn_bwd_noalloc",
@@ -70,6 +71,58 @@ def fwd(L, q=None, k=None, v=None, o=None, lse=None, Bsz=1, N=128, Hq=8, Hkv=2, 
 ])
 def test_fwd_validation(L, kw, code):
     assert fwd(L, **kw) == code
+
+
+def fwd_ws(L, ws=None, ws_bytes=None, **kw):
+    p = dict(Bsz=1, N=8192, Hq=8, Hkv=2, d=128, scale=0.088, causal=1, dtype=B.UL_BF16)
+    p.update(kw)
+    need = L.ul_attn_fwd_workspace_bytes(p["Bsz"], p["N"], p["Hq"], p["Hkv"], p["d"], p["dtype"])
+    ptrs = [addr(i) for i in range(5)]
+    for i, n in enumerate(["q", "k", "v", "o", "lse"]):
+        if n in p:
+            ptrs[i] = p.pop(n)
+    ws = addr(9) if ws is None else ws
+    return L.ul_attn_fwd_ws(*ptrs, ws, need if ws_bytes is None else ws_bytes, p["Bsz"], p["N"],
+                            p["Hq"], p["Hkv"], p["d"], p["scale"], p["causal"], p["dtype"], None)
+
+
+def test_fwd_workspace_bytes(L):
+    # N=8192, 8 query / 2 KV heads: 64-row query blocks, 128 per lane, the upper 64 split in
+    # two; per split half 8 waves x 32 rows of d fp32 outputs plus (m, l)
+    rows = 2 * 64 * 2 * 256
+    assert L.ul_attn_fwd_workspace_bytes(1, 8192, 8, 2, 128, B.UL_BF16) == rows * (128 * 4 + 8)
+    assert L.ul_attn_fwd_workspace_bytes(1, 8192, 8, 2, 64, B.UL_BF16) == rows * (64 * 4 + 8)
+    # one KV head: 256 blocks of one lane still split
+    assert L.ul_attn_fwd_workspace_bytes(1, 16384, 4, 1, 128, B.UL_BF16) == 128 * 2 * 256 * 520
+    # MHA: 256-row query blocks; 4 lanes x 64 blocks split, 4 x 128 do not
+    assert L.ul_attn_fwd_workspace_bytes(1, 16384, 4, 4, 128, B.UL_BF16) == 4 * 32 * 2 * 256 * 520
+    assert L.ul_attn_fwd_workspace_bytes(1, 32768, 4, 4, 128, B.UL_BF16) == 0
+    # more than 256 items (long N, more heads or batch), too few blocks, fp32, invalid sizes
+    assert L.ul_attn_fwd_workspace_bytes(1, 65536, 8, 2, 128, B.UL_BF16) == 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 8193, 8, 2, 128, B.UL_BF16) == 0
+    assert L.ul_attn_fwd_workspace_bytes(2, 8192, 8, 2, 128, B.UL_BF16) == 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 8192, 32, 8, 128, B.UL_BF16) == 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 960, 8, 2, 128, B.UL_BF16) == 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 1024, 8, 2, 128, B.UL_BF16) > 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 8192, 8, 2, 128, B.UL_F32) == 0
+    assert L.ul_attn_fwd_workspace_bytes(1, 8192, 6, 4, 128, B.UL_BF16) == 0
+    # the largest split: 256 items
+    assert max(L.ul_attn_fwd_workspace_bytes(b, n, hq, hkv, 128, B.UL_BF16)
+               for b in (1, 2, 4) for n in range(1024, 70000, 1024)
+               for hq, hkv in ((8, 2), (4, 4), (4, 1), (2, 2))) <= 256 * 256 * 520
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=ctypes.c_void_p(0)), 1),
+    (dict(ws=ctypes.c_void_p(0)), 6), (dict(ws_bytes=16), 6),
+    (dict(ws=ctypes.c_void_p(A + 9 * BIG + 8)), 5),
+    (dict(ws=ctypes.c_void_p(A + 2 * BIG + 4096)), 7),   # workspace inside v
+    (dict(ws=ctypes.c_void_p(A + 3 * BIG + 4096)), 7),   # workspace inside o
+    (dict(ws=ctypes.c_void_p(A + 4 * BIG)), 7),          # workspace at lse
+    (dict(Hq=6, Hkv=4), 3), (dict(d=80), 4), (dict(N=0), 2),
+])
+def test_fwd_ws_validation(L, kw, code):
+    assert fwd_ws(L, **kw) == code
 
 
 def bwd(L, ws_bytes=None, ws=None, stages=None, **kw):

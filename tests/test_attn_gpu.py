@@ -112,6 +112,57 @@ def test_shape_sweep_full_parity(Bsz, N, Hq, Hkv, d, dtype, causal):
     _compare_full(gpu, _oracle_full(st, dtype, scale, causal), dtype, label)
 
 
+# ---------------------------------------------------------------------------- split key range
+
+
+SPLIT_SWEEP = [
+    # (B, N, Hq, Hkv, d): query blocks of 64 rows (4+ query heads per KV head), 128 rows (2)
+    # or 256 rows (1); 16 .. 128 blocks, ragged last blocks
+    (1, 1000, 8, 2, 128),
+    (1, 2100, 4, 2, 128),
+    (1, 4100, 2, 2, 64),
+    (2, 1500, 8, 2, 64),
+    (1, 8192, 8, 1, 128),
+]
+
+
+@pytest.mark.parametrize("Bsz,N,Hq,Hkv,d", SPLIT_SWEEP)
+def test_split_forward_matches_oracle(Bsz, N, Hq, Hkv, d):
+    """ul_attn_fwd_ws, which runs the upper query blocks as two key-range halves combined
+    afterwards, and ul_attn_fwd, which does not, both against the float64 oracle on every
+    row; a NaN-filled workspace and NaN-poisoned outputs must leave no trace."""
+    B = _B()
+    label = f"split B{Bsz}-N{N}-{Hq}q{Hkv}kv-d{d}"
+    print(f"[parity] {label}", flush=True)
+    need = B.fwd_workspace_bytes(Bsz, N, Hq, Hkv, d, B.UL_BF16)
+    assert need > 0, "these sizes are meant to split"
+    st = synth.custom_inputs(Bsz, N, Hq, Hkv, d, "bf16", seed=N * 11 + Hq, with_dout=False)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (H.to_device(st[n], "bf16") for n in ("q", "k", "v"))
+    ws = torch.full((need // 4,), float("nan"), device="cuda").view(torch.uint8)
+    res = {}
+    for split in (True, False):
+        o = torch.full_like(q, float("nan"))
+        lse = torch.full((Bsz, Hq, N), float("nan"), device="cuda")
+        B.attn_fwd(q, k, v, scale, True, out=o, lse=lse, split=split, workspace=ws if split else None)
+        torch.cuda.synchronize()
+        res[split] = (H.to_f64(o), H.to_f64(lse))
+    w = H.widen_inputs(st, "bf16")
+    o_ref, lse_ref = OA.attn_fwd(w["q"], w["k"], w["v"], scale, True)
+    for split, (o, lse) in res.items():
+        assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{label} split={split}"
+        H.check_o_bf16(o, o_ref, f"{label} O split={split}")
+        H.check_max_abs(lse, lse_ref, H.TOL_BF16_LSE, f"{label} lse split={split}")
+    # the lower half of the query blocks is never split: bit-identical on both paths, and the
+    # split rows differ from the unsplit ones only by rounding
+    grp = Hq // Hkv
+    rows_per_blk = 32 * 8 // (4 if grp % 4 == 0 else 2 if grp % 2 == 0 else 1)
+    lo = (-(-N // rows_per_blk) + 1) // 2 * rows_per_blk
+    assert np.array_equal(res[True][0][:, :lo], res[False][0][:, :lo]), f"{label}: unsplit rows differ"
+    assert np.array_equal(res[True][1][:, :, :lo], res[False][1][:, :, :lo]), f"{label}: unsplit lse differ"
+    assert not np.array_equal(res[True][0][:, lo:], res[False][0][:, lo:]), f"{label}: split path not taken"
+
+
 # ---------------------------------------------------------------------------- large N, sampled
 
 

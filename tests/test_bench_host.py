@@ -12,6 +12,7 @@ import pytest
 ROOT = Path(__file__).resolve().parents[1]
 sys.path.insert(0, str(ROOT))
 import bench  # noqa: E402
+from ulysses_sequence_parallelism_attn_amd import synth  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -42,7 +43,8 @@ def test_ingest_scales_by_the_first_calibration_copy(tmp_path):
                     [(cal, 524288.0), (fwd, 1000.0), (fwd, 3000.0), (dkdv, 10.0), (cal, 7.0)])
     _write_counters(tmp_path / "W", "WRITE_SIZE",
                     [(cal, 1048576.0), (fwd, 100.0), (fwd, 300.0), (dkdv, 1.0), (cal, 9.0)])
-    rec = bench.ingest_pmc(str(tmp_path / "F"), str(tmp_path / "W"))
+    rec = bench.ingest_pmc(str(tmp_path / "F"), str(tmp_path / "W"), "wl-x")
+    assert rec["workload"] == "wl-x"
     assert rec["calibration"]["fetch_factor"] == pytest.approx(2.0)
     assert rec["calibration"]["write_factor"] == pytest.approx(1.0)
     # per launch: the mean over dispatches, in KiB, times 1024 and the factor
@@ -56,16 +58,20 @@ def test_ingest_scales_by_the_first_calibration_copy(tmp_path):
 
 def test_traffic_is_reported_only_for_the_measured_sources(tmp_path, monkeypatch):
     f = tmp_path / "traffic.json"
-    f.write_text(json.dumps({"kernel_hash": bench.kernel_hash(), "bytes_per_launch": {"attn_fwd": 5.0}}))
+    f.write_text(json.dumps({"kernel_hash": bench.kernel_hash(), "workload": "wl-a",
+                             "bytes_per_launch": {"attn_fwd": 5.0}}))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", f)
-    assert bench.measured_traffic("attn_fwd") == 5.0
-    assert bench.measured_traffic("attn_bwd_dq") is None
-    f.write_text(json.dumps({"kernel_hash": "0" * 16, "bytes_per_launch": {"attn_fwd": 5.0}}))
-    assert bench.measured_traffic("attn_fwd") is None
+    assert bench.measured_traffic("attn_fwd", "wl-a") == 5.0
+    assert bench.measured_traffic("attn_bwd_dq", "wl-a") is None
+    assert bench.measured_traffic("attn_fwd", "wl-b") is None  # another workload's bytes
+    f.write_text(json.dumps({"kernel_hash": "0" * 16, "workload": "wl-a",
+                             "bytes_per_launch": {"attn_fwd": 5.0}}))
+    assert bench.measured_traffic("attn_fwd", "wl-a") is None
     f.write_text("not json")
-    assert bench.measured_traffic("attn_fwd") is None
+    assert bench.measured_traffic("attn_fwd", "wl-a") is None
 
 
 def test_committed_traffic_matches_the_kernel_sources():
     rec = json.loads(bench.TRAFFIC_FILE.read_text())
     assert rec["kernel_hash"] == bench.kernel_hash(), "profiles/traffic.json is stale: re-run the counter passes"
+    assert rec["workload"] == synth.WORKLOADS[3].name

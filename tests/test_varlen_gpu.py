@@ -94,8 +94,9 @@ def test_varlen_full_parity(dtype, lengths, Hq, Hkv, d, causal):
 
 
 def test_varlen_metric_size_matches_per_sequence_calls():
-    """65536 packed tokens of the seeded length mix equal the plain call on each sequence:
-    O, lse and dQ bit for bit.  dK and dV to 1e-3 relative L2: a plain call on a sequence
+    """65536 packed tokens of the seeded length mix equal the plain call on each sequence
+    (its forward without the key-range split, which packed calls do not take): O, lse and
+    dQ bit for bit.  dK and dV to 1e-3 relative L2: a plain call on a sequence
     this short runs its longest key blocks one query head at a time and sums the heads'
     fp32 partials afterwards, a different summation order from the packed call's (which the
     float64 oracle checks on its own in test_varlen_full_parity)."""
@@ -117,7 +118,7 @@ def test_varlen_metric_size_matches_per_sequence_calls():
     for s in range(len(lengths)):
         a, b = int(cu[s]), int(cu[s + 1])
         sl = lambda t: t[a:b][None].contiguous()
-        o1, l1 = B.attn_fwd(sl(q), sl(k), sl(v), scale, True)
+        o1, l1 = B.attn_fwd(sl(q), sl(k), sl(v), scale, True, split=False)
         dq1, dk1, dv1 = B.attn_bwd(sl(q), sl(k), sl(v), o1, sl(do), l1, scale, True)
         torch.cuda.synchronize()
         for name, x, r in (("o", o[a:b], o1[0]), ("dq", dq[a:b], dq1[0]), ("lse", lse[:, a:b], l1[0])):

@@ -56,6 +56,11 @@ def lib() -> ctypes.CDLL:
         L.ul_attn_fwd_strided.argtypes = ([vp] * 5 + [i64, i64, i32, i32, i32] + [i64] * 4 +
                                           [f32, i32, i32, vp])
         L.ul_attn_fwd_strided.restype = ctypes.c_int
+        L.ul_attn_fwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
+        L.ul_attn_fwd_workspace_bytes.restype = sz
+        L.ul_attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, i32, f32, i32,
+                                     i32, vp]
+        L.ul_attn_fwd_ws.restype = ctypes.c_int
         L.ul_attn_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
         L.ul_attn_bwd_workspace_bytes.restype = sz
         L.ul_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i32, i32,
@@ -256,12 +261,20 @@ def _tok_stride(t, name: str) -> int:
     return ts
 
 
+def fwd_workspace_bytes(B, N, Hq, Hkv, d, dtype_code) -> int:
+    return int(lib().ul_attn_fwd_workspace_bytes(B, N, Hq, Hkv, d, dtype_code))
+
+
 def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None, lse=None,
-             stream=None):
+             stream=None, split: bool = True, workspace=None):
     """O, lse = attention(q, k, v).  q [B,N,Hq,d], k/v [B,N,Hkv,d] (bf16 or fp32).
 
     q, k, v and `out` may be views with a token stride (for example a rank's head slice
     of a sequence-sharded [B,N,H,d] tensor); heads and head dim must be dense.
+    With `split` (dense tensors only), sizes for which fwd_workspace_bytes is non-zero run
+    through ul_attn_fwd_ws, which splits the key range of the longest query blocks; the
+    workspace is allocated here unless given.  split=False runs ul_attn_fwd, whose
+    rounding the strided and varlen calls share.
     """
     import torch
 
@@ -276,7 +289,15 @@ def attn_fwd(q, k, v, scale: float | None = None, causal: bool = True, out=None,
     ts = [_tok_stride(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "out"))]
     head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse_t), B, N, Hq, Hkv, d)
     tail = (scale, int(causal), _dtype_code(q), _stream(stream))
-    if all(t.is_contiguous() for t in (q, k, v, o)):
+    dense = all(t.is_contiguous() for t in (q, k, v, o))
+    need = fwd_workspace_bytes(B, N, Hq, Hkv, d, _dtype_code(q)) if split and dense else 0
+    if need > 0:
+        if workspace is None:
+            workspace = _internal_workspace(need, q.device, stream)
+        check_workspace(workspace, need, q)
+        _check("ul_attn_fwd_ws", lib().ul_attn_fwd_ws(*head[:5], _ptr(workspace), workspace.numel(),
+                                                      *head[5:], *tail))
+    elif dense:
         _check("ul_attn_fwd", lib().ul_attn_fwd(*head, *tail))
     else:
         _check("ul_attn_fwd_strided", lib().ul_attn_fwd_strided(*head, *ts, *tail))

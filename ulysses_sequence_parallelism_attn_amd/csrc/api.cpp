@@ -251,7 +251,8 @@ ul_status check_seqs(const Seqs &sq, int64_t total) {
 ul_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
                    int64_t N, int32_t Hq, int32_t Hkv, int32_t head_dim, const int64_t ts[4],
                    float softmax_scale, int32_t causal, int32_t dtype, void *stream,
-                   const Seqs *seqs) {
+                   const Seqs *seqs, bool with_ws = false, void *workspace = nullptr,
+                   size_t workspace_bytes = 0) {
     if (!q || !k || !v || !o || !lse) return UL_ERR_NULL;
     AttnSizes sz;
     ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
@@ -265,13 +266,18 @@ ul_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
         (st = check_tensor(o, ts[3], T, Hq, head_dim, es, &ro)) != UL_OK)
         return st;
     if (!aligned16(lse)) return UL_ERR_ALIGNMENT;
+    AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
+    // the workspace is needed only where the sizes split the key range
+    const size_t need = with_ws ? ul::attn_fwd_workspace_bytes(s, dtype) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return UL_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return UL_ERR_ALIGNMENT;
     const Rows rl = dense(lse, sz.lse_bytes);
+    const Rows rw = dense(need > 0 ? workspace : nullptr, (int64_t)need);
     const Rows rc = seqs ? dense(seqs->cu, ((int64_t)seqs->n + 1) * 4) : dense(nullptr, 0);
-    for (const Rows &out : {ro, rl})
+    for (const Rows &out : {ro, rl, rw})
         for (const Rows &in : {rq, rk, rv, rc})
             if (intersects(out, in)) return UL_ERR_OVERLAP;
-    if (intersects(ro, rl)) return UL_ERR_OVERLAP;
-    AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};
+    if (intersects(ro, rl) || intersects(ro, rw) || intersects(rl, rw)) return UL_ERR_OVERLAP;
     s.q_rs = ts[0];
     s.k_rs = ts[1];
     s.v_rs = ts[2];
@@ -288,7 +294,7 @@ ul_status fwd_impl(const void *q, const void *k, const void *v, void *o, float *
                                                 static_cast<const float *>(k),
                                                 static_cast<const float *>(v),
                                                 static_cast<float *>(o), lse, s, hs));
-    return from_hip(ul::launch_attn_fwd_bf16(q, k, v, o, lse, s, hs));
+    return from_hip(ul::launch_attn_fwd_bf16(q, k, v, o, lse, need > 0 ? workspace : nullptr, s, hs));
 }
 
 struct BwdStrides {
@@ -415,6 +421,24 @@ ul_status ul_attn_fwd(const void *q, const void *k, const void *v, void *o, floa
     const int64_t ts[4] = {qs, kvs, kvs, qs};
     return fwd_impl(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype,
                     stream, nullptr);
+}
+
+size_t ul_attn_fwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv,
+                                   int32_t head_dim, int32_t dtype) {
+    AttnSizes sz;
+    if (check_attn(B, N, Hq, Hkv, head_dim, 1.0f, 1, dtype, &sz) != UL_OK) return 0;
+    const AttnShape s{B, N, Hq, Hkv, head_dim, 1.0f, 1};
+    return ul::attn_fwd_workspace_bytes(s, dtype);
+}
+
+ul_status ul_attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                         void *workspace, size_t workspace_bytes, int64_t B, int64_t N, int32_t Hq,
+                         int32_t Hkv, int32_t head_dim, float softmax_scale, int32_t causal,
+                         int32_t dtype, void *stream) {
+    const int64_t qs = (int64_t)Hq * head_dim, kvs = (int64_t)Hkv * head_dim;
+    const int64_t ts[4] = {qs, kvs, kvs, qs};
+    return fwd_impl(q, k, v, o, lse, B, N, Hq, Hkv, head_dim, ts, softmax_scale, causal, dtype,
+                    stream, nullptr, true, workspace, workspace_bytes);
 }
 
 ul_status ul_attn_fwd_varlen(const void *q, const void *k, const void *v, void *o, float *lse,

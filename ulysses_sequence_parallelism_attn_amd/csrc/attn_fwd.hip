@@ -71,7 +71,42 @@ struct FwdParams {
     int32_t n_qblk;         // ceil(N / (32 * pos_blocks))
     float scale_log2;       // softmax_scale * log2(e)
     int32_t causal;
+    // Split key range (shorter causal sequences): query blocks split_from ..
+    // n_qblk-1 run as two work items, one over the first half of their key
+    // tiles and one over the rest, each writing its unnormalised fp32 O and
+    // (running max, sum) to part_o / part_ml; fwd_merge_kernel combines them.
+    // split_from = n_qblk: no split.
+    int32_t split_from;
+    float *part_o, *part_ml;
 };
+
+// The work items of one lane (b, KV head, head group) when the upper query
+// blocks are split: cycles of the two halves of two split blocks followed by
+// one whole block, all taken from the longest down, so that the dispatch
+// order stays close to longest-first (a split half of block i has about
+// (i+1)/2 tiles, a whole block j has j+1, and the cycle keeps the two in
+// step); then the last split block if their count is odd, then the remaining
+// whole blocks.  Returns the query block; `chunk` is 0 / 1 for the halves and
+// -1 for a whole block.
+__device__ __forceinline__ int fwd_split_item(int u, int n, int K, int &chunk) {
+    const int S = n - K, C = S / 2, odd = S % 2;
+    if (u < 5 * C) {
+        const int c = u / 5, r = u % 5;
+        if (r < 4) {
+            chunk = r % 2;
+            return n - 1 - 2 * c - r / 2;
+        }
+        chunk = -1;
+        return K - 1 - c;
+    }
+    u -= 5 * C;
+    if (odd && u < 2) {
+        chunk = u;
+        return K;
+    }
+    chunk = -1;
+    return K - 1 - C - (u - 2 * odd);
+}
 
 template <int D>
 struct FwdTile {
@@ -234,12 +269,15 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // ---- work item, longest first: item = rank * (B*Hkv*head_groups) + rest
     const int per_rank = p.B * p.Hkv * p.head_groups;
     const int rank = blockIdx.x / per_rank;
-    int rest = blockIdx.x - rank * per_rank;
+    const int lane_id = blockIdx.x - rank * per_rank;
+    int rest = lane_id;
     const int g = rest % p.Hkv;
     rest /= p.Hkv;
     const int hg = rest % p.head_groups;
     const int b = rest / p.head_groups;
-    const int qblk = p.causal ? (p.n_qblk - 1 - rank) : rank;
+    int chunk = -1;
+    const int qblk = p.split_from < p.n_qblk ? fwd_split_item(rank, p.n_qblk, p.split_from, chunk)
+                                             : (p.causal ? (p.n_qblk - 1 - rank) : rank);
     const SeqRange sq = seq_range(p.cu_seqlens, b, p.N, p.Hq, p.total);
 
     const int grp = p.Hq / p.Hkv;
@@ -270,10 +308,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     acc.m = -INFINITY;
     acc.l = 0.f;
 
-    // tiles [0, n_full) are visible to every row of the workgroup and inside N
+    // tiles [0, n_full) are visible to every row of the workgroup and inside N;
+    // this item takes tiles [ta, tb): all of them, or one half of a split
+    // block's (the first half lies inside [0, n_full))
     const int kend = p.causal ? min(N, wg_pos0 + wg_rows) : N;
-    const int ntiles = (kend + kKT - 1) / kKT;
-    const int n_full = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
+    const int ntiles_all = (kend + kKT - 1) / kKT;
+    const int n_full_all = p.causal ? min(wg_pos0, N) / kKT : N / kKT;
+    const int half = ntiles_all / 2;
+    const int ta = chunk == 1 ? half : 0;
+    const int ntiles = chunk == 0 ? half : ntiles_all;
+    const int n_full = chunk == 0 ? min(half, n_full_all) : n_full_all;
     const float c = p.scale_log2;
     // Absolute LDS addresses: the lane's fragment offsets plus the LDS base
     // (and, for V, the V region); the empty asm keeps the compiler from
@@ -340,9 +384,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // t+1); each wave waits for its share of tile t+1 before the barrier that
     // ends its MFMA half of tile t, which is before anyone reads it.
     const bool lagging = wave >= kWaves / 2;
-    issue(0, lds + T::k_stage(0));
-    if (ntiles > 1) {
-        issue(1, lds + T::k_stage(1));
+    // stages follow the tile index relative to the item's first tile
+    issue(ta, lds + T::k_stage(0));
+    if (ntiles - ta > 1) {
+        issue(ta + 1, lds + T::k_stage(1));
         wait_vm_barrier<kDmaPerWave>();
     } else {
         wait_vm_barrier<0>();
@@ -372,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
         } else {
             if (more) issue(t + 2, nx);
             auto none = [](int) {};
-            if (t >= 1 && visible(t - 1))
+            if (t >= ta + 1 && visible(t - 1))
                 fwd_gemm<D, true, false, 0>(acc, pf, s, qf, ring, stage(t - 1), 0, fo, none);
             if (t < ntiles && visible(t)) fwd_gemm<D, false, true, 0>(acc, pf, s, qf, ring, 0, stage(t), fo, none);
         }
@@ -396,12 +441,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // fours so that every stage offset is a constant, then the rest (at most
     // three unmasked tiles, the masked ones and the last PV) with computed
     // stages and the masking softmax, which is exact on unmasked tiles too.
-    auto rt_stage = [](int x) { return (uint32_t)T::k_stage(x & (T::kStages - 1)); };
-    body(0, std::false_type{}, rt_stage);
-    int t0 = 1;
+    auto rt_stage = [ta](int x) { return (uint32_t)T::k_stage((x - ta) & (T::kStages - 1)); };
+    body(ta, std::false_type{}, rt_stage);
+    int t0 = ta + 1;
     for (; t0 + T::kStages <= n_full; t0 += T::kStages) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
             // x - t0 + 1 folds to a constant for every tile index body derives from t0 + J
+            // (t0 - ta is 1 modulo the stage count, as the run-time stages assume)
             (body(t0 + J, std::true_type{},
                   [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
              ...);
@@ -412,6 +458,25 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
 
     // ---- epilogue: normalise, round to bf16, write O and lse
     const float ltot = half_sum(acc.l);
+    if (chunk >= 0) {  // half of a split block: unnormalised O and (m, l), fp32
+        const int64_t slot = ((int64_t)lane_id * (p.n_qblk - p.split_from) + (qblk - p.split_from)) * 2 + chunk;
+        const int64_t rw = (slot * kWaves + wave) * kRowsPerWave + m;
+        float *po = p.part_o + rw * D;
+#pragma unroll
+        for (int eb = 0; eb < EB; ++eb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 ov;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ov[q] = acc.o[eb][r4 * 4 + q];
+                *reinterpret_cast<f32x4 *>(po + eb * 32 + r4 * 8 + kg * 4) = ov;
+            }
+        if (kg == 0) {
+            p.part_ml[rw * 2] = acc.m;
+            p.part_ml[rw * 2 + 1] = ltot;
+        }
+        return;
+    }
     if (row < N) {
         const float inv = 1.f / ltot;
         uint16_t *orow = p.o + (sq.tok0 + row) * p.o_rs + (int64_t)h * D;
@@ -426,6 +491,50 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
             }
         if (kg == 0) p.lse[sq.lse0 + (int64_t)h * sq.hs + row] = (acc.m + __log2f(ltot)) * kLn2;
     }
+}
+
+// Combines the two halves of each split query block (the key ranges [0, h)
+// and [h, end) of every row): with m_c, l_c and the unnormalised O_c of half
+// c, all relative to 2^m_c,
+//   M = max(m_0, m_1),  a_c = 2^(m_c - M),
+//   o = (a_0 O_0 + a_1 O_1) / (a_0 l_0 + a_1 l_1),  lse = (M + log2 l) ln 2,
+// the same online-softmax update the kernel applies between key tiles.  One
+// thread per 4 dimensions of a row; rows past N are skipped.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams p, int64_t n_threads) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= n_threads) return;
+    constexpr int Q = D / 4;
+    const int dq = (int)(t % Q);
+    const int64_t r = t / Q;  // (pair, wave, m)
+    const int m = (int)(r % kRowsPerWave);
+    const int wave = (int)((r / kRowsPerWave) % kWaves);
+    const int64_t pair = r / (kRowsPerWave * kWaves);  // lane_id * S + split block
+    const int S = p.n_qblk - p.split_from;
+    const int lane_id = (int)(pair / S);
+    const int qblk = p.split_from + (int)(pair % S);
+    const int g = lane_id % p.Hkv;
+    const int hg = (lane_id / p.Hkv) % p.head_groups;
+    const int b = lane_id / (p.Hkv * p.head_groups);
+    const int h = g * (p.Hq / p.Hkv) + hg * p.heads_per_wg + wave % p.heads_per_wg;
+    const int row = qblk * kRowsPerWave * p.pos_blocks + (wave / p.heads_per_wg) * kRowsPerWave + m;
+    if (row >= p.N) return;
+    const int64_t rw0 = ((pair * 2) * kWaves + wave) * kRowsPerWave + m;
+    const int64_t rw1 = rw0 + kWaves * kRowsPerWave;
+    const float m0 = p.part_ml[rw0 * 2], l0 = p.part_ml[rw0 * 2 + 1];
+    const float m1 = p.part_ml[rw1 * 2], l1 = p.part_ml[rw1 * 2 + 1];
+    const float mm = fmaxf(m0, m1);
+    const float a0 = exp2f(m0 - mm), a1 = exp2f(m1 - mm);  // one of them is 1
+    const float l = a0 * l0 + a1 * l1;
+    const float inv = 1.f / l;
+    const f32x4 o0 = *reinterpret_cast<const f32x4 *>(p.part_o + rw0 * D + dq * 4);
+    const f32x4 o1 = *reinterpret_cast<const f32x4 *>(p.part_o + rw1 * D + dq * 4);
+    bf16x4 ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(fmaf(a0, o0[e], a1 * o1[e]) * inv);
+    const int64_t tok = (int64_t)b * p.N + row;
+    *reinterpret_cast<u32x2 *>(p.o + tok * p.o_rs + (int64_t)h * D + dq * 4) = __builtin_bit_cast(u32x2, ov);
+    if (dq == 0) p.lse[((int64_t)b * p.Hq + h) * p.N + row] = (mm + __log2f(l)) * kLn2;
 }
 
 // ============================================================================ fp32 kernel
@@ -512,10 +621,57 @@ __global__ __launch_bounds__(kF32Rows) void attn_fwd_f32_kernel(FwdF32Params p) 
     }
 }
 
+// Work decomposition of one bf16 call.  The key range of the upper half of
+// the query blocks is split in two when the call has at most kSplitMaxItems
+// work items (one per query block of each lane): with about one item per CU
+// the longest-first order cannot balance the CUs, since the last block holds
+// twice the mean work, and halving the longest items fixes most of that.
+// With more items the order balances by itself and the partials' round trip
+// costs more than it gains (measured: N=8192 with 8 query / 2 KV heads, 256
+// items, forward 203 -> 174 us; with 32 / 8 heads, 1024 items, 502 -> 558 us).
+// The partials take at most kSplitMaxItems x 2 x 256 rows x (4 d + 8) bytes,
+// 34 MB at d = 128.
+constexpr int64_t kSplitMaxItems = 256;
+constexpr int kSplitMinBlocks = 16;  // a split block keeps >= 8 key tiles, its first half unmasked
+
+struct FwdPlan {
+    int32_t heads_per_wg, pos_blocks, head_groups, n_qblk, split_from;
+    int64_t lanes;
+    size_t part_o_bytes, part_ml_bytes;
+};
+
+FwdPlan fwd_plan(const AttnShape &s, int32_t dtype) {
+    FwdPlan pl{};
+    const int grp = s.Hq / s.Hkv;
+    pl.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
+    pl.pos_blocks = kWaves / pl.heads_per_wg;
+    pl.head_groups = grp / pl.heads_per_wg;
+    const int64_t pos_per_wg = (int64_t)kRowsPerWave * pl.pos_blocks;
+    pl.n_qblk = (int32_t)((s.N + pos_per_wg - 1) / pos_per_wg);
+    pl.split_from = pl.n_qblk;
+    pl.lanes = s.B * s.Hkv * pl.head_groups;
+    if (dtype != 1 || !s.causal || s.cu || pl.n_qblk < kSplitMinBlocks ||
+        pl.lanes * pl.n_qblk > kSplitMaxItems)
+        return pl;
+    const int32_t K = (pl.n_qblk + 1) / 2;
+    const int64_t slots = pl.lanes * (pl.n_qblk - K) * 2;
+    const size_t rows = (size_t)slots * kWaves * kRowsPerWave;
+    const size_t ob = rows * s.d * 4, mb = rows * 2 * 4;
+    pl.split_from = K;
+    pl.part_o_bytes = ob;
+    pl.part_ml_bytes = mb;
+    return pl;
+}
+
 }  // namespace
 
+size_t attn_fwd_workspace_bytes(const AttnShape &s, int32_t dtype) {
+    const FwdPlan pl = fwd_plan(s, dtype);
+    return pl.part_o_bytes + pl.part_ml_bytes;
+}
+
 hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
-                                const AttnShape &s, hipStream_t stream) {
+                                void *ws, const AttnShape &s, hipStream_t stream) {
     FwdParams p;
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(k);
@@ -532,25 +688,35 @@ hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, voi
     p.o_rs = s.o_rs;
     p.cu_seqlens = s.cu;
     p.total = s.total;
-    const int grp = s.Hq / s.Hkv;
-    p.heads_per_wg = (grp % 4 == 0) ? 4 : (grp % 2 == 0) ? 2 : 1;
-    p.pos_blocks = kWaves / p.heads_per_wg;
-    p.head_groups = grp / p.heads_per_wg;
-    const int64_t pos_per_wg = (int64_t)kRowsPerWave * p.pos_blocks;
-    p.n_qblk = (int32_t)((s.N + pos_per_wg - 1) / pos_per_wg);
+    // a null workspace runs the call unsplit
+    const FwdPlan pl = fwd_plan(s, 1);
+    p.heads_per_wg = pl.heads_per_wg;
+    p.pos_blocks = pl.pos_blocks;
+    p.head_groups = pl.head_groups;
+    p.n_qblk = pl.n_qblk;
     p.scale_log2 = s.scale * kLog2e;
     p.causal = s.causal;
-    const int64_t items = (int64_t)p.n_qblk * p.B * p.Hkv * p.head_groups;
+    const bool split = ws && pl.split_from < pl.n_qblk;
+    p.split_from = split ? pl.split_from : pl.n_qblk;
+    p.part_o = split ? static_cast<float *>(ws) : nullptr;
+    p.part_ml = split ? reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + pl.part_o_bytes) : nullptr;
+    // items per lane: every query block once, the split ones twice
+    const int64_t per_lane = (int64_t)p.n_qblk + (p.n_qblk - p.split_from);
+    const int64_t items = per_lane * pl.lanes;
     if (items <= 0) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((uint32_t)items), block(kThreads);
+    const int64_t merge_threads = pl.lanes * (p.n_qblk - p.split_from) * kWaves * kRowsPerWave * (s.d / 4);
+    const dim3 mgrid((uint32_t)((merge_threads + 255) / 256));
     hipError_t err;
     if (s.d == 128) {
         if ((err = allow_lds(attn_fwd_bf16_kernel<128>, FwdTile<128>::kLds)) != hipSuccess) return err;
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, FwdTile<128>::kLds, stream, p);
+        if (split) hipLaunchKernelGGL(fwd_merge_kernel<128>, mgrid, dim3(256), 0, stream, p, merge_threads);
     } else {
         if ((err = allow_lds(attn_fwd_bf16_kernel<64>, FwdTile<64>::kLds)) != hipSuccess) return err;
         hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, FwdTile<64>::kLds, stream, p);
+        if (split) hipLaunchKernelGGL(fwd_merge_kernel<64>, mgrid, dim3(256), 0, stream, p, merge_threads);
     }
     return hipGetLastError();
 }

@@ -109,8 +109,11 @@ struct AttnShape {
 
 hipError_t launch_attn_fwd_f32(const float *q, const float *k, const float *v, float *o,
                                float *lse, const AttnShape &s, hipStream_t stream);
+// Device workspace of the bf16 forward's split key range (0 when these sizes
+// run unsplit); launch_attn_fwd_bf16 with a null `ws` runs unsplit.
+size_t attn_fwd_workspace_bytes(const AttnShape &s, int32_t dtype);
 hipError_t launch_attn_fwd_bf16(const void *q, const void *k, const void *v, void *o, float *lse,
-                                const AttnShape &s, hipStream_t stream);
+                                void *ws, const AttnShape &s, hipStream_t stream);
 
 size_t attn_bwd_workspace_bytes(const AttnShape &s, int32_t dtype);
 hipError_t launch_attn_bwd_f32(const float *q, const float *k, const float *v, const float *o,
