@@ -120,10 +120,13 @@ constexpr int kQWaves = 8;
 constexpr int kQThreads = kQWaves * 64;
 constexpr int kRowsPerWave = 32;
 constexpr int kDqKT = 32;   // keys per tile
-// A fragments read ahead of their MFMA: 6, but no more than the dQ steps of
+// A fragments read ahead of their MFMA: 4, and no more than the dQ steps of
 // a tile, since the prefetch at the end of the softmax half covers only those.
+// (6 ahead measured the same for the standalone kernel at N = 65536, but it
+// left the kernel holding both backward passes at 256 registers with 49
+// spilled; 4 removes the spills and took 9 % off that kernel at N = 8192.)
 template <int D>
-constexpr int kQAhead = 2 * (D / 32) < 6 ? 2 * (D / 32) : 6;
+constexpr int kQAhead = 2 * (D / 32) < 4 ? 2 * (D / 32) : 4;
 
 struct DqParams {
     const uint16_t *q, *k, *v, *dout;
