@@ -410,6 +410,34 @@ def varlen_step(B, torch, synth, q, k, v, do, wl, args) -> dict:
             "counted_flop": flops}
 
 
+def graph_step(torch, step, args, ms_eager) -> dict:
+    """The same step (the calls of `step`, without its per-stage events) captured once in a
+    HIP graph and replayed: the library allocates, synchronises and memsets nothing, so the
+    whole step is one graph launch per iteration."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(args.warmup):
+        g.replay()
+    stream = torch.cuda.current_stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    del g
+    return {"ms_per_step": ms, "time_vs_eager": ms / ms_eager}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +451,8 @@ def main() -> int:
                     help="skip the packed variable-length variant of the step")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the head-chunked variant of the step")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip the device-copy reference for the relayout's bytes")
     ap.add_argument("--cpu-prefix", type=int, default=16384)
@@ -627,6 +657,8 @@ def main() -> int:
         "bwd_launch": "dq+dkdv merged" if merged_bwd else "dq, dkdv separate",
         "fwd_split": bool(fws_bytes),
     }
+    if not args.no_graph:
+        out["graph"] = graph_step(torch, step, args, ms_per_step)
     if not args.no_copy_ceiling:
         out["copy_ceiling"] = copy_ceiling(torch, x)
     if not args.no_fused:
