@@ -29,8 +29,9 @@
 // exactness path).
 
 #include <algorithm>
-#include <type_traits>
 #include <utility>
+#include <vector>
+#include <type_traits>
 
 #include "mfma_tile.h"
 #include "ul_internal.h"
@@ -1104,19 +1105,67 @@ __global__ __launch_bounds__(256) void dkdv_reduce_kernel(DkvParams p) {
 }
 
 // Both backward passes in one launch, for grids too small to fill the chip
-// on their own (short sequences): the dK/dV work items (the longer ones)
-// first, then the dQ items, so the two passes share the compute units instead
-// of each leaving part of them idle.  Each workgroup runs exactly the body of
-// the standalone kernel for its item.  (Interleaving the two families in
-// proportion to their counts measured 2-4 % slower at N = 8192 and 16384.)
+// on their own (short sequences), so the two passes share the compute units
+// instead of each leaving part of them idle.  Each workgroup runs exactly the
+// body of the standalone kernel for its item.  The items run in the order
+// `order` gives, longest first over both families (the host estimates each
+// item's length, see merged_order); without it (use_order = 0) the dK/dV
+// items run first, then the dQ items.
 static_assert(kQThreads == kKvThreads, "one block size for both passes");
+constexpr int kMergedMaxItems = 1024;
+constexpr uint16_t kMergedDq = 0x8000;  // item code: dQ item (low bits: its index), else dK/dV
+struct MergedOrder {
+    uint16_t item[kMergedMaxItems];
+};
 template <int D>
 __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_dkdv_bf16_kernel(DqParams dp, DkvParams kp,
-                                                                           int kv_items) {
-    if ((int)blockIdx.x < kv_items)
-        dkdv_body<D>(kp, blockIdx.x);
+                                                                           int kv_items, MergedOrder order,
+                                                                           int use_order) {
+    int code;
+    if (use_order)
+        code = order.item[blockIdx.x];
     else
-        dq_body<D>(dp, blockIdx.x - kv_items);
+        code = (int)blockIdx.x < kv_items ? (int)blockIdx.x : (kMergedDq | ((int)blockIdx.x - kv_items));
+    if (!(code & kMergedDq))
+        dkdv_body<D>(kp, code);
+    else
+        dq_body<D>(dp, code & ~kMergedDq);
+}
+
+// Longest first over both families of the merged launch: each item's length
+// estimated from its steps (32 query rows of a 128-key block for one head,
+// dK/dV) or tiles (32 keys for all rows of a dQ block), weighted 3 : 4, their
+// measured costs at N = 65536 (0.89 and 1.20 us).  A stable sort keeps each
+// family's own longest-first order among equal estimates.  Causal, equal-
+// length sequences only (packed ones have lengths only the device knows);
+// false when the grid is too large for the table.
+bool merged_order(const DqParams &dp, const DkvParams &kp, int kv_items, int dq_items, MergedOrder *out) {
+    if (!kp.causal || kp.cu_seqlens || kv_items + dq_items > kMergedMaxItems) return false;
+    const int64_t nqt = ((int64_t)kp.N + kQT - 1) / kQT;
+    const int grp = kp.Hq / kp.Hkv;
+    const int kv_lanes = kp.B * kp.Hkv;
+    const int n_split = kp.ksplit * kv_lanes * grp;
+    std::vector<std::pair<int64_t, uint16_t>> items;
+    items.reserve(kv_items + dq_items);
+    for (int i = 0; i < kv_items; ++i) {
+        const bool split = i < n_split;
+        const int kblk = split ? i / (kv_lanes * grp) : kp.ksplit + (i - n_split) / kv_lanes;
+        const int64_t steps = (nqt - (int64_t)kblk * (kKeysPerWg / kQT)) * (split ? 1 : grp);
+        items.push_back({3 * steps, (uint16_t)i});
+    }
+    const int dq_lanes = dp.B * dp.Hkv * dp.head_groups;
+    const int64_t wg_rows = (int64_t)kRowsPerWave * dp.pos_blocks;
+    for (int i = 0; i < dq_items; ++i) {
+        const int qblk = dp.n_qblk - 1 - i / dq_lanes;
+        const int64_t keys = std::min<int64_t>(dp.N, (qblk + 1) * wg_rows);
+        items.push_back({4 * ((keys + kDqKT - 1) / kDqKT), (uint16_t)(kMergedDq | i)});
+    }
+    std::stable_sort(items.begin(), items.end(),
+                     [](const std::pair<int64_t, uint16_t> &a, const std::pair<int64_t, uint16_t> &b) {
+                         return a.first > b.first;
+                     });
+    for (size_t r = 0; r < items.size(); ++r) out->item[r] = items[r].second;
+    return true;
 }
 
 // ============================================================================ fp32 kernels
@@ -1442,18 +1491,20 @@ hipError_t launch_attn_bwd_bf16(const void *q, const void *k, const void *v, con
             return err;
         if ((int64_t)kp.n_kblk * kp.B * kp.Hkv < 4 * (int64_t)cus) {
             const dim3 grid((uint32_t)(kv_items + dq_items)), block(kKvThreads);
+            MergedOrder order;
+            const int use_order = merged_order(dp, kp, (int)kv_items, (int)dq_items, &order) ? 1 : 0;
             if (s.d == 128) {
                 constexpr size_t lds = DqTile<128>::kLds > DkvTile<128>::kLds ? DqTile<128>::kLds
                                                                               : DkvTile<128>::kLds;
                 if ((err = allow_lds(attn_bwd_dq_dkdv_bf16_kernel<128>, lds)) != hipSuccess) return err;
                 hipLaunchKernelGGL(attn_bwd_dq_dkdv_bf16_kernel<128>, grid, block, lds, stream, dp, kp,
-                                   (int)kv_items);
+                                   (int)kv_items, order, use_order);
             } else {
                 constexpr size_t lds = DqTile<64>::kLds > DkvTile<64>::kLds ? DqTile<64>::kLds
                                                                             : DkvTile<64>::kLds;
                 if ((err = allow_lds(attn_bwd_dq_dkdv_bf16_kernel<64>, lds)) != hipSuccess) return err;
                 hipLaunchKernelGGL(attn_bwd_dq_dkdv_bf16_kernel<64>, grid, block, lds, stream, dp, kp,
-                                   (int)kv_items);
+                                   (int)kv_items, order, use_order);
             }
             if ((err = hipGetLastError()) != hipSuccess) return err;
             return reduce();
