@@ -30,7 +30,6 @@
 
 #include <algorithm>
 #include <utility>
-#include <vector>
 #include <type_traits>
 
 #include "mfma_tile.h"
@@ -1135,36 +1134,44 @@ __global__ __launch_bounds__(kKvThreads) void attn_bwd_dq_dkdv_bf16_kernel(DqPar
 // Longest first over both families of the merged launch: each item's length
 // estimated from its steps (32 query rows of a 128-key block for one head,
 // dK/dV) or tiles (32 keys for all rows of a dQ block), weighted 3 : 4, their
-// measured costs at N = 65536 (0.89 and 1.20 us).  A stable sort keeps each
-// family's own longest-first order among equal estimates.  Causal, equal-
-// length sequences only (packed ones have lengths only the device knows);
-// false when the grid is too large for the table.
+// measured costs at N = 65536 (0.89 and 1.20 us).  The head-split dK/dV
+// items, the whole dK/dV items and the dQ items are each already in
+// decreasing order of that estimate, so the order is their merge, taking the
+// earlier family on ties (the result of a stable sort of the three in that
+// order); no allocation.  Causal, equal-length sequences only (packed ones
+// have lengths only the device knows); false when the grid is too large for
+// the table.
 bool merged_order(const DqParams &dp, const DkvParams &kp, int kv_items, int dq_items, MergedOrder *out) {
     if (!kp.causal || kp.cu_seqlens || kv_items + dq_items > kMergedMaxItems) return false;
     const int64_t nqt = ((int64_t)kp.N + kQT - 1) / kQT;
     const int grp = kp.Hq / kp.Hkv;
     const int kv_lanes = kp.B * kp.Hkv;
     const int n_split = kp.ksplit * kv_lanes * grp;
-    std::vector<std::pair<int64_t, uint16_t>> items;
-    items.reserve(kv_items + dq_items);
-    for (int i = 0; i < kv_items; ++i) {
-        const bool split = i < n_split;
-        const int kblk = split ? i / (kv_lanes * grp) : kp.ksplit + (i - n_split) / kv_lanes;
-        const int64_t steps = (nqt - (int64_t)kblk * (kKeysPerWg / kQT)) * (split ? 1 : grp);
-        items.push_back({3 * steps, (uint16_t)i});
-    }
     const int dq_lanes = dp.B * dp.Hkv * dp.head_groups;
     const int64_t wg_rows = (int64_t)kRowsPerWave * dp.pos_blocks;
-    for (int i = 0; i < dq_items; ++i) {
+    auto kv_cost = [&](int i) {  // i < kv_items
+        const bool split = i < n_split;
+        const int kblk = split ? i / (kv_lanes * grp) : kp.ksplit + (i - n_split) / kv_lanes;
+        return 3 * (nqt - (int64_t)kblk * (kKeysPerWg / kQT)) * (split ? 1 : grp);
+    };
+    auto dq_cost = [&](int i) {  // i < dq_items
         const int qblk = dp.n_qblk - 1 - i / dq_lanes;
         const int64_t keys = std::min<int64_t>(dp.N, (qblk + 1) * wg_rows);
-        items.push_back({4 * ((keys + kDqKT - 1) / kDqKT), (uint16_t)(kMergedDq | i)});
+        return 4 * ((keys + kDqKT - 1) / kDqKT);
+    };
+    // cursors: head-split dK/dV items [0, n_split), whole ones [n_split, kv_items), dQ items
+    int a = 0, w = std::min(n_split, kv_items), q = 0;
+    for (int r = 0; r < kv_items + dq_items; ++r) {
+        const int64_t ca = a < std::min(n_split, kv_items) ? kv_cost(a) : -1;
+        const int64_t cw = w < kv_items ? kv_cost(w) : -1;
+        const int64_t cq = q < dq_items ? dq_cost(q) : -1;
+        if (ca >= cw && ca >= cq)
+            out->item[r] = (uint16_t)a++;
+        else if (cw >= cq)
+            out->item[r] = (uint16_t)w++;
+        else
+            out->item[r] = (uint16_t)(kMergedDq | q++);
     }
-    std::stable_sort(items.begin(), items.end(),
-                     [](const std::pair<int64_t, uint16_t> &a, const std::pair<int64_t, uint16_t> &b) {
-                         return a.first > b.first;
-                     });
-    for (size_t r = 0; r < items.size(); ++r) out->item[r] = items[r].second;
     return true;
 }
 
