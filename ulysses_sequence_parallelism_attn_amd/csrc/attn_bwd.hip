@@ -298,11 +298,6 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     const int64_t so = sq.st0 + (int64_t)h * 2 * sq.hs + (ok ? row : 0);
     const float cn = ok ? p.stats[so] * p.scale_log2 : 0.f;  // -lse log2(e)
     const float nDrow = ok ? p.stats[so + sq.hs] : 0.f;     // -D
-    f32x16 nd;  // the dP^T accumulator's starting value
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nd[r] = nDrow;
-    // Retire these loads: inside the loop vmcnt counts only the tile loads.
-    __builtin_amdgcn_s_waitcnt(0x70);
 
     f32x16 dqacc[EB];
 #pragma unroll
@@ -371,8 +366,15 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     // t+1); each wave waits for its share of tile t+1 before the barrier
     // ending its MFMA half of tile t (all but the 5 newest tiles' loads).
     const bool lagging = wave >= kQWaves / 2;
+    // The Q/dO/statistics loads above stay in flight while the first tiles'
+    // loads are issued: loads retire in order, so the wait for tile 0 retires
+    // them too, and every later wait (at most k of the newest loads
+    // outstanding) still counts only tile loads.
     for (int t = 0; t < T::kAhead; ++t)
         if (t < ntiles) issue(t, lds + T::k_stage(t));
+    f32x16 nd;  // the dP^T accumulator's starting value
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nd[r] = nDrow;
     if (ntiles >= T::kAhead)
         wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
     else
@@ -416,6 +418,12 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     };
     auto rt_stage = [](int x) { return (uint32_t)T::k_stage(x & (T::kStages - 1)); };
     body(0, std::false_type{}, rt_stage);
+    // The unmasked tiles 1 .. n_full-1 on the unrolled path: whole groups of
+    // kStages in a straight loop, then one group that stops at n_full.  Every
+    // group starts at a tile that is 1 modulo the stage count, so each of its
+    // stage offsets is a constant.  The run-time-stage path below costs about
+    // twice as much per tile (2.0 against 1.1 us at N = 65536), and a test
+    // after every tile inside the main loop slows it by 1.5-3 %.
     int t0 = 1;
     for (; t0 + T::kStages <= n_full; t0 += T::kStages) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
@@ -424,6 +432,16 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
                   [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
              ...);
         }(std::make_integer_sequence<int, T::kStages>{});
+    }
+    if (t0 < n_full) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            ((t0 + J < n_full &&
+              (body(t0 + J, std::true_type{},
+                    [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+               true)) &&
+             ...);
+        }(std::make_integer_sequence<int, T::kStages - 1>{});
+        t0 = n_full;
     }
     for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage);
     if (!lagging) fence_barrier();
@@ -761,8 +779,19 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // step the producer works on re-reads of the last step's tiles with every
     // element masked, and what it stores is never read.
     const int niter = nsteps + 2;
+    // Whole groups in a straight loop, then the rest in a loop whose
+    // iterations each test the count (a test per iteration inside the main
+    // loop costs ~1 %).  The rest is a loop although it runs at most once:
+    // its back edge keeps the reads that follow each P/dS hand-over live in
+    // the compiled code, which the hand-over wait counts on.
     auto run = [&](auto iter) {
-        for (int i0 = 0; i0 < niter; i0 += T::kStages) {
+        int i0 = 0;
+        for (; i0 + T::kStages <= niter; i0 += T::kStages) {
+            [&]<int... J>(std::integer_sequence<int, J...>) {
+                (iter(std::integral_constant<int, J>{}), ...);
+            }(std::make_integer_sequence<int, T::kStages>{});
+        }
+        for (; i0 < niter; i0 += T::kStages) {
             [&]<int... J>(std::integer_sequence<int, J...>) {
                 ((i0 + J < niter ? iter(std::integral_constant<int, J>{}) : void()), ...);
             }(std::make_integer_sequence<int, T::kStages>{});
