@@ -348,15 +348,25 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
         dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
     }
-    auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
+    // The tile the next loads fetch, set up by dma_prep one body ahead (at
+    // the end of the dS half, off the MFMA stream): the address of its first
+    // key row (wave-uniform) and the byte offset of its last row inside N, so
+    // that a load in the MFMA stream is a clamp, an add and the M0 write.
+    const uint32_t dma_lds = (uint32_t)(uintptr_t)lds + tile_lds + u0 * 1024;
+    const uint16_t *dma_tb = tens;
+    uint32_t dma_lim = 0;
+    auto dma_prep = [&](int t) {
         const int j0 = t * kDqKT;
-        const uint32_t lim = (uint32_t)min(N - 1 - j0, kDqKT) * row_bytes;  // last key of the sequence
-        dma_b128(tens + (int64_t)j0 * t_rs, min(dma_roff[k], lim) + dma_gran[k],
-                 base + tile_lds + (u0 + k) * 1024);
+        dma_tb = uniform_ptr(tens + (int64_t)j0 * t_rs);
+        dma_lim = (uint32_t)max(min(N - 1 - j0, kDqKT), 0) * row_bytes;  // last key of the sequence
     };
-    auto issue = [&](int t, UL_LDS unsigned char *base) {
+    // load k of this wave's share of the prepared tile into the stage at byte offset `st`
+    auto issue_k = [&](int k, uint32_t st) {
+        dma_b128_m0(dma_tb, min(dma_roff[k], dma_lim) + dma_gran[k], dma_lds + st + k * 1024);
+    };
+    auto issue = [&](uint32_t st) {
 #pragma unroll
-        for (int k = 0; k < kDmaPerWave; ++k) issue_k(t, k, base);
+        for (int k = 0; k < kDmaPerWave; ++k) issue_k(k, st);
     };
     auto visible = [&](int t) { return !p.causal || t * kDqKT <= i0 + kRowsPerWave - 1; };
 
@@ -371,7 +381,10 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     // them too, and every later wait (at most k of the newest loads
     // outstanding) still counts only tile loads.
     for (int t = 0; t < T::kAhead; ++t)
-        if (t < ntiles) issue(t, lds + T::k_stage(t));
+        if (t < ntiles) {
+            dma_prep(t);
+            issue(T::k_stage(t));
+        }
     f32x16 nd;  // the dP^T accumulator's starting value
 #pragma unroll
     for (int r = 0; r < 16; ++r) nd[r] = nDrow;
@@ -379,22 +392,22 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
     else
         wait_vm_barrier<0>();
+    dma_prep(T::kAhead);
     if (lagging) fence_barrier();
 
     f32x16 s, dp;
     bf16x8 dsf[2];
     bf16x8 ring[kQAhead<D>];
-    auto body = [&](int t, auto full, auto stage) {
+    auto body = [&](int t, auto full, auto stage, uint32_t stage_next) {  // stage_next: tile t+kAhead's
         constexpr bool FULL = decltype(full)::value;
         const bool more = t + T::kAhead < ntiles;
-        UL_LDS unsigned char *nx = lds + stage(t + T::kAhead);
         if constexpr (FULL) {
             dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), stage(t), fo,
                                                 [&](int k) {
-                                                    if (more) issue_k(t + T::kAhead, k, nx);
+                                                    if (more) issue_k(k, stage_next);
                                                 });
         } else {
-            if (more) issue(t + T::kAhead, nx);
+            if (more) issue(stage_next);
             auto none = [](int) {};
             if (t >= 1 && visible(t - 1))
                 dq_gemm<D, true, false, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), 0, fo, none);
@@ -414,10 +427,11 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
                 dq_ds<true>(dsf, s, dp, cn, kg, t * kDqKT, row, N, p.causal, c);
             dq_prefetch<D>(ring, stage(t), fo);
         }
+        dma_prep(t + T::kAhead + 1);  // the tile the next body loads
         fence_barrier();
     };
     auto rt_stage = [](int x) { return (uint32_t)T::k_stage(x & (T::kStages - 1)); };
-    body(0, std::false_type{}, rt_stage);
+    body(0, std::false_type{}, rt_stage, rt_stage(T::kAhead));
     // The unmasked tiles 1 .. n_full-1 on the unrolled path: whole groups of
     // kStages in a straight loop, then one group that stops at n_full.  Every
     // group starts at a tile that is 1 modulo the stage count, so each of its
@@ -429,7 +443,8 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
             // x - t0 + 1 folds to a constant for every tile index body derives from t0 + J
             (body(t0 + J, std::true_type{},
-                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); },
+                  (uint32_t)T::k_stage((J + 1 + T::kAhead) & (T::kStages - 1))),
              ...);
         }(std::make_integer_sequence<int, T::kStages>{});
     }
@@ -437,13 +452,14 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
             ((t0 + J < n_full &&
               (body(t0 + J, std::true_type{},
-                    [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+                    [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); },
+                    (uint32_t)T::k_stage((J + 1 + T::kAhead) & (T::kStages - 1))),
                true)) &&
              ...);
         }(std::make_integer_sequence<int, T::kStages - 1>{});
         t0 = n_full;
     }
-    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage);
+    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage, rt_stage(t + T::kAhead));
     if (!lagging) fence_barrier();
 
     // dQ = scale * (dQ^T)^T, rounded to bf16: lane column = query row, registers = head dim

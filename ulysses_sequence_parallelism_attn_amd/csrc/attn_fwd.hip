@@ -357,16 +357,27 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
         dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
         dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
     }
-    // load k of this wave's share of tile t into the stage at `base`
-    auto issue_k = [&](int t, int k, UL_LDS unsigned char *base) {
+    // The tile the next loads fetch, set up by dma_prep one body ahead (at
+    // the end of the softmax half, off the MFMA stream): the address of its
+    // first key row (wave-uniform) and the byte offset of its last row inside
+    // N.  A load in the MFMA stream is then a clamp, an add and the M0 write;
+    // computing the address there took ~17 scalar instructions per load,
+    // which held back the MFMAs behind them.
+    const uint32_t dma_lds = (uint32_t)(uintptr_t)lds + tile_lds + u0 * 1024;
+    const uint16_t *dma_tb = tens;
+    uint32_t dma_lim = 0;
+    auto dma_prep = [&](int t) {
         const int j0 = t * kKT;
-        const uint32_t lim = (uint32_t)min(N - 1 - j0, kKT) * row_bytes;  // last key of the sequence
-        dma_b128(tens + (int64_t)j0 * t_rs, min(dma_roff[k], lim) + dma_gran[k],
-                 base + tile_lds + (u0 + k) * 1024);
+        dma_tb = uniform_ptr(tens + (int64_t)j0 * t_rs);
+        dma_lim = (uint32_t)max(min(N - 1 - j0, kKT), 0) * row_bytes;  // last key of the sequence
     };
-    auto issue = [&](int t, UL_LDS unsigned char *base) {
+    // load k of this wave's share of the prepared tile into the stage at byte offset `st`
+    auto issue_k = [&](int k, uint32_t st) {
+        dma_b128_m0(dma_tb, min(dma_roff[k], dma_lim) + dma_gran[k], dma_lds + st + k * 1024);
+    };
+    auto issue = [&](uint32_t st) {
 #pragma unroll
-        for (int k = 0; k < kDmaPerWave; ++k) issue_k(t, k, base);
+        for (int k = 0; k < kDmaPerWave; ++k) issue_k(k, st);
     };
     // tile t holds keys this wave's rows can see
     auto visible = [&](int t) { return !p.causal || t * kKT <= i0 + kRowsPerWave - 1; };
@@ -385,13 +396,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // ends its MFMA half of tile t, which is before anyone reads it.
     const bool lagging = wave >= kWaves / 2;
     // stages follow the tile index relative to the item's first tile
-    issue(ta, lds + T::k_stage(0));
+    dma_prep(ta);
+    issue(T::k_stage(0));
     if (ntiles - ta > 1) {
-        issue(ta + 1, lds + T::k_stage(1));
+        dma_prep(ta + 1);
+        issue(T::k_stage(1));
         wait_vm_barrier<kDmaPerWave>();
     } else {
         wait_vm_barrier<0>();
     }
+    dma_prep(ta + 2);
     if (lagging) fence_barrier();
 
     f32x16 s[2];
@@ -402,20 +416,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // first V fragments of the next MFMA half.  `stage(x)` is tile x's stage
     // offset.  FULL: both tiles take part and tile t is unmasked (the steady
     // state, one straight block); otherwise each part is checked on its own.
-    auto body = [&](int t, auto full, auto stage) {
+    auto body = [&](int t, auto full, auto stage, uint32_t stage2) {  // stage2: tile t+2's
         constexpr bool FULL = decltype(full)::value;
         const bool more = t + 2 < ntiles;
-        UL_LDS unsigned char *nx = lds + stage(t + 2);
         // The wave feeding the MFMA pipe takes issue priority over the other
         // wave of its SIMD (busy with its softmax) until its half ends.
         __builtin_amdgcn_s_setprio(2);
         if constexpr (FULL) {
             fwd_gemm<D, true, true, kDmaPerWave>(acc, pf, s, qf, ring, stage(t - 1), stage(t), fo,
                                                  [&](int k) {
-                                                     if (more) issue_k(t + 2, k, nx);
+                                                     if (more) issue_k(k, stage2);
                                                  });
         } else {
-            if (more) issue(t + 2, nx);
+            if (more) issue(stage2);
             auto none = [](int) {};
             if (t >= ta + 1 && visible(t - 1))
                 fwd_gemm<D, true, false, 0>(acc, pf, s, qf, ring, stage(t - 1), 0, fo, none);
@@ -435,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
                 fwd_softmax<D, true>(acc, s, pf, kg, t * kKT, row, N, p.causal, c);
             fwd_prefetch<D>(ring, stage(t), fo);
         }
+        dma_prep(t + 3);  // the tile the next body loads
         fence_barrier();
     };
     // Tile 0 (no PV yet), then the whole unmasked tiles 1 .. n_full-1 in
@@ -442,18 +456,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_bf16_kernel(FwdParams p) {
     // three unmasked tiles, the masked ones and the last PV) with computed
     // stages and the masking softmax, which is exact on unmasked tiles too.
     auto rt_stage = [ta](int x) { return (uint32_t)T::k_stage((x - ta) & (T::kStages - 1)); };
-    body(ta, std::false_type{}, rt_stage);
+    body(ta, std::false_type{}, rt_stage, rt_stage(ta + 2));
     int t0 = ta + 1;
     for (; t0 + T::kStages <= n_full; t0 += T::kStages) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
             // x - t0 + 1 folds to a constant for every tile index body derives from t0 + J
             // (t0 - ta is 1 modulo the stage count, as the run-time stages assume)
             (body(t0 + J, std::true_type{},
-                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); }),
+                  [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); },
+                  (uint32_t)T::k_stage((J + 3) & (T::kStages - 1))),
              ...);
         }(std::make_integer_sequence<int, T::kStages>{});
     }
-    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage);
+    for (int t = t0; t <= ntiles; ++t) body(t, std::false_type{}, rt_stage, rt_stage(t + 2));
     if (!lagging) fence_barrier();
 
     // ---- epilogue: normalise, round to bf16, write O and lse
