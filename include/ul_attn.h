@@ -222,8 +222,10 @@ size_t ul_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t Hq, int32_t Hkv
  *               bytes, caller-owned, 16-byte aligned; its contents on entry
  *               do not matter and are scratch afterwards.
  * Deterministic: no atomics; identical inputs give bit-identical outputs.
- * Errors: as ul_attn_fwd, plus WORKSPACE, and OVERLAP when dq, dk, dv or the
- * workspace overlap each other or any input.
+ * Errors: as ul_attn_fwd, plus WORKSPACE, OVERLAP when dq, dk, dv or the
+ * workspace overlap each other or any input, and SHAPE for BF16 with
+ * N >= 2^30 (total_tokens for packed sequences: the statistics are addressed
+ * with 32-bit offsets; no such problem fits one GPU's memory).
  */
 ul_status ul_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                       const void *dout, const float *lse, void *dq, void *dk, void *dv,

@@ -345,6 +345,8 @@ def noalloc(L, **kw):
     (dict(dq=ctypes.c_void_p(A + 8)), 5),
     (dict(dk=ctypes.c_void_p(A + 64)), 7),            # dk overlaps q
     (dict(N=1 << 23), 9), (dict(Bsz=9, N=1 << 20, Hq=4, Hkv=1), 9),  # beyond the fixed scratch
+    # bf16 statistics are addressed with 32-bit offsets: N < 2^30 (fp32 is not limited)
+    (dict(N=1 << 30, Hq=1, Hkv=1, d=64), 2), (dict(N=1 << 30, Hq=1, Hkv=1, d=64, dtype=B.UL_F32), 9),
 ])
 def test_noalloc_validation(L, kw, code):
     """ul_attn_bwd_noalloc validates before touching the runtime; a problem whose statistics

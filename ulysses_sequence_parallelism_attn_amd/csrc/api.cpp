@@ -316,6 +316,9 @@ ul_status bwd_impl(int32_t stages, const void *q, const void *k, const void *v, 
     AttnSizes sz;
     ul_status st = check_attn(B, N, Hq, Hkv, head_dim, softmax_scale, causal, dtype, &sz);
     if (st != UL_OK) return st;
+    // the bf16 dK/dV kernel addresses the -D half of its statistics (N floats,
+    // or total for packed sequences, past the -lse half) with a 32-bit offset
+    if (dtype == UL_BF16 && N >= (int64_t(1) << 30)) return UL_ERR_SHAPE;
     if (seqs && (st = check_seqs(*seqs, N)) != UL_OK) return st;
     if (stages < 1 || (stages & ~UL_BWD_ALL) != 0) return UL_ERR_UNSUPPORTED;
     AttnShape s{B, N, Hq, Hkv, head_dim, softmax_scale, causal};

@@ -401,6 +401,9 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     auto body = [&](int t, auto full, auto stage, uint32_t stage_next) {  // stage_next: tile t+kAhead's
         constexpr bool FULL = decltype(full)::value;
         const bool more = t + T::kAhead < ntiles;
+        // The wave feeding the MFMA pipe takes issue priority over the other
+        // wave of its SIMD (busy with its dS) until its half ends.
+        __builtin_amdgcn_s_setprio(2);
         if constexpr (FULL) {
             dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), stage(t), fo,
                                                 [&](int k) {
@@ -415,6 +418,7 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
                 dq_gemm<D, false, true, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, 0, stage(t), fo, none);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         if (more)
             wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
         else
@@ -941,24 +945,21 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // The loads of a step, issued together: this consumer's share of the Q or
     // dO tile of step `cu` into stage st, and on the last consumer the 32
     // rows' -lse/scale (lanes 0-31) and -D (lanes 32-63, one statistics block
-    // later), one dword per lane.  `trow` / `srow` point at head 0 of the
-    // group at the step's first row; head hi adds hi * D elements (hi * 2 hs
-    // statistics).  Rows past N re-read row N-1 (masked by the producers).
+    // later), one dword per lane in one instruction.  `trow` / `srow` point at
+    // the step's first row of the step's head.  Rows past N re-read row N-1
+    // (masked by the producers).  The -D half's offset, hs * 4 bytes, fits the
+    // 32-bit lane offset: the launcher rejects statistics strides of 2^30.
     const int64_t head_stride_st = 2 * sq.hs;
+    const uint32_t stat_off = lane < kQT ? 0u : (uint32_t)sq.hs * 4u;
     // load k of the step (k = kDmaPerWave: the statistics, last consumer only)
     auto issue_k = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st, int k) {
         const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
         if (k < kDmaPerWave) {
-            dma_b128_m0(trow + cu.hi * D, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
+            dma_b128_m0(trow, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
                         lbase + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
-        } else if (stats_wave) {  // two loads, one per half of the wave, each from a uniform base
-            const float *sl = srow + cu.hi * head_stride_st;
+        } else if (stats_wave) {
             const int r = min(lane & (kQT - 1), lim);
-            const uint32_t sdst = lbase + T::kStatBase + T::stat_stage(st);
-            if (lane < kQT)
-                dma_b32_m0(sl, (uint32_t)r * 4, sdst);
-            else
-                dma_b32_m0(sl + sq.hs, (uint32_t)r * 4, sdst);
+            dma_b32_m0(srow, (uint32_t)r * 4 + stat_off, lbase + T::kStatBase + T::stat_stage(st));
         }
     };
     auto issue = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st) {
@@ -973,29 +974,36 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // A stage is rewritten three iterations after the consumers' last read
     // of it (step t-3's stage takes step t+3; step t-3 was consumed in
     // iteration t-1, whose reads its MFMAs waited for).
-    auto wait_next = [&]() {
+    auto wait_next = [&]() {  // this iteration's loads: kDmaPerWave, and the statistics on the last consumer
         if (stats_wave)
-            wait_vm_only<kDmaPerWave + 2>();
+            wait_vm_only<kDmaPerWave + 1>();
         else
             wait_vm_only<kDmaPerWave>();
     };
-    // The cursor of the step to load next, with its row pointers.
-    const uint16_t *trow0 = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)(g * grp + h0) * D;
-    const float *srow0 = p.stats + sq.st0 + (int64_t)(g * grp + h0) * head_stride_st + first.r0;
+    // The cursor of the step to load next, with its row pointers: at the
+    // group's first head (trb / srb) and at the step's head (trow / srow), so
+    // that no load multiplies by the head index.
+    const uint16_t *trb = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)(g * grp + h0) * D;
+    const float *srb = p.stats + sq.st0 + (int64_t)(g * grp + h0) * head_stride_st + first.r0;
     const int64_t trow_step = (int64_t)kQT * t_rs;
-    auto advance_load = [&](Cur &cu, const uint16_t *&trow, const float *&srow) {
-        const int r0 = cu.r0;
+    const uint16_t *trow = trb;
+    const float *srow = srb;
+    auto advance_load = [&](Cur &cu) {
+        const int r0 = cu.r0, hi = cu.hi;
         advance(cu);
         if (cu.r0 != r0) {
-            trow -= trow_step;
-            srow -= kQT;
+            trb -= trow_step;
+            srb -= kQT;
+            trow = trb;
+            srow = srb;
+        } else if (cu.hi != hi) {
+            trow += D;
+            srow += head_stride_st;
         }
     };
     Cur iss = first;
-    const uint16_t *trow = trow0;
-    const float *srow = srow0;
     [&]<int... J>(std::integer_sequence<int, J...>) {
-        ((issue(iss, trow, srow, J), advance_load(iss, trow, srow)), ...);
+        ((issue(iss, trow, srow, J), advance_load(iss)), ...);
     }(std::make_integer_sequence<int, T::kAhead>{});
     wait_vm<0>();  // the first steps have landed
     fence_barrier();
@@ -1044,7 +1052,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             }
         cons.template run<kDmaPerWave + 1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV),
                                            [&](int k) { issue_k(iss, trow, srow, NN, k); });
-        advance_load(iss, trow, srow);
+        advance_load(iss);
         cons.prefetch(ring, T::q_stage(NX));
         wait_next();
         fence_barrier();
