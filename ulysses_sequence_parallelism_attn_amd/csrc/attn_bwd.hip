@@ -880,12 +880,18 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         };
 
         fence_barrier();  // the consumers' first loads have landed
-        // Set 0 starts as step 0; set 1 holds "step -1": P = exp2(-inf) = 0, dS = 0.
-        f32x16 s[2], dp[2];
+        // Three register sets rotate: step t accumulates in set t % 3, the
+        // softmax of step t-1 reads set (t-1) % 3, and the starting values of
+        // step t+1 are loaded straight into set (t+1) % 3, whose step t-2 is
+        // done, so no copy is needed (the stage count, 6, keeps every index a
+        // constant).  Set 0 starts as step 0; set 2 holds "step -1":
+        // P = exp2(-inf) = 0, dS = 0.
+        static_assert(T::kStages % 3 == 0, "register sets rotate with the stages");
+        f32x16 s[3], dp[3];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            s[1][r] = -INFINITY;
-            dp[1][r] = 0.f;
+            s[2][r] = -INFINITY;
+            dp[2][r] = 0.f;
         }
         bf16x8 ring[kKvAhead];
         dkdv_inits(s[0], dp[0], stat + T::stat_stage(0));
@@ -893,17 +899,16 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
         run([&](auto J) {
             constexpr int ST = decltype(J)::value;          // stage of step t
-            constexpr int A = ST % 2, Bs = (ST + 1) % 2;    // accumulator sets of steps t and t-1 (then t+1)
+            constexpr int A = ST % 3, Pv = (ST + 2) % 3;    // register sets of steps t and t-1
+            constexpr int X = (ST + 1) % 3;                 // set of step t+1 (step t-2's, done)
             constexpr int NX = (ST + 1) % T::kStages;       // stage of step t+1
             constexpr int PB = (ST + 1) % 2;                // P/dS buffer of step t-1
-            f32x16 sn, nn;  // starting values of step t+1, loaded halfway through the stream
-            dkdv_producer_iter<D>(s[A], dp[A], s[Bs], dp[Bs], kf, vf, ring, T::q_stage(ST), oq, od,
+            // the starting values of step t+1 are loaded halfway through the stream
+            dkdv_producer_iter<D>(s[A], dp[A], s[Pv], dp[Pv], kf, vf, ring, T::q_stage(ST), oq, od,
                                   pds + PB * T::kPds, c,
-                                  [&]() { dkdv_inits(sn, nn, stat + T::stat_stage(NX)); });
-            s[Bs] = sn;
-            dp[Bs] = nn;
+                                  [&]() { dkdv_inits(s[X], dp[X], stat + T::stat_stage(NX)); });
             next_step();
-            prepare(s[Bs]);
+            prepare(s[X]);
             dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
             // P / dS of step t-1 stored before the barrier; the next step's
             // operand reads may stay in flight across it (they are waited for
