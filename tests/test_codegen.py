@@ -2,7 +2,8 @@
 
 Before the barrier that hands its P / dS fragments to the consumers, a dK/dV producer waits
 only until its own P / dS writes have retired, and leaves the LDS reads it issued after them
-in flight (`s_waitcnt lgkmcnt(K)` rather than lgkmcnt(0)).  That retires every write only
+in flight (`s_waitcnt lgkmcnt(K)` rather than lgkmcnt(0); the same instruction may also wait on
+the producer's own tile loads, `vmcnt(n)`).  That retires every write only
 while the compiled code keeps three facts, which this test checks in the assembly of every
 kernel that contains the producer (the dK/dV kernels and the merged backward kernel,
 head_dim 64 and 128):
@@ -44,7 +45,7 @@ def _kernels(text):
     """Lines of each dK/dV-containing kernel, by symbol (labels kept: they end basic blocks)."""
     out = {}
     for m in re.finditer(r"^(_Z\S*dkdv_bf16_kernel\S*):", text, re.M):
-        body = text[m.end():text.index("s_endpgm", m.end())]
+        body = text[m.end():text.index(".Lfunc_end", m.end())]  # every exit of the kernel
         out[m.group(1)] = [ln.strip() for ln in body.split("\n")
                            if ln.strip() and not ln.strip().startswith((";", ".p2align", ".loc", ".file"))]
     return out
@@ -76,8 +77,8 @@ def test_producer_waits_retire_exactly_the_pds_writes(asm):
     for name, ins in kernels.items():
         # the producer's hand-over waits: lgkmcnt(K) right before a barrier (a
         # compiler-placed wait with the same count elsewhere guards a register use)
-        waits = [i for i, x in enumerate(ins)
-                 if x == f"s_waitcnt lgkmcnt({K})" and ins[i + 1].startswith("s_barrier")]
+        wait = re.compile(rf"^s_waitcnt (vmcnt\(\d+\) )?lgkmcnt\({K}\)$")
+        waits = [i for i, x in enumerate(ins) if wait.match(x) and ins[i + 1].startswith("s_barrier")]
         checked = 0
         for i in waits:
             # the straight-line code that every path runs right before the wait: back to

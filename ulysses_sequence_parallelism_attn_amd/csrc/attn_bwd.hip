@@ -454,12 +454,12 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     }
     if (t0 < n_full) {
         [&]<int... J>(std::integer_sequence<int, J...>) {
-            ((t0 + J < n_full &&
-              (body(t0 + J, std::true_type{},
-                    [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); },
-                    (uint32_t)T::k_stage((J + 1 + T::kAhead) & (T::kStages - 1))),
-               true)) &&
-             ...);
+            (void)((t0 + J < n_full &&
+                    (body(t0 + J, std::true_type{},
+                          [t0](int x) { return (uint32_t)T::k_stage((x - t0 + 1) & (T::kStages - 1)); },
+                          (uint32_t)T::k_stage((J + 1 + T::kAhead) & (T::kStages - 1))),
+                     true)) &&
+                   ...);
         }(std::make_integer_sequence<int, T::kStages - 1>{});
         t0 = n_full;
     }
@@ -530,6 +530,12 @@ constexpr int kKvAhead = 6;                          // A fragments read ahead o
 // before the barrier lets this many stay outstanding, which retires every
 // write before them.
 constexpr int kReadsAfterPds = kKvAhead;
+// S MFMAs of step t+1 that a producer issues at the end of iteration t, ahead
+// of the barrier: step t+1's tiles and starting values are published by then,
+// and the MFMAs keep the matrix pipe busy while both roles meet at the barrier.
+// Two measured as well as four, six or seven at d=128; two also fits d=64,
+// where the prefetch has to stay within one step.
+constexpr int kEarly = 2;
 
 struct DkvParams {
     const uint16_t *q, *k, *v, *dout;
@@ -581,11 +587,13 @@ __device__ __forceinline__ bf16x8 dkdv_sdp_frag(int st, uint32_t qst, const uint
     return lds_frag_at((st < KK ? oq[st] : od[st - KK]) + qst);
 }
 
+// The first kKvAhead fragments of a producer iteration: fragments kEarly ..
+// of the step (its first kEarly S MFMAs were issued in the iteration before).
 template <int D>
 __device__ __forceinline__ void dkdv_sdp_prefetch(bf16x8 (&ring)[kKvAhead], uint32_t qst, const uint32_t *oq,
                                                   const uint32_t *od) {
 #pragma unroll
-    for (int st = 0; st < kKvAhead; ++st) ring[st] = dkdv_sdp_frag<D>(st, qst, oq, od);
+    for (int st = 0; st < kKvAhead; ++st) ring[st] = dkdv_sdp_frag<D>(st + kEarly, qst, oq, od);
 }
 
 // The starting values of step t+1's accumulators for this lane's 16 rows
@@ -629,13 +637,17 @@ __device__ __forceinline__ void dkdv_mask_init(f32x16 &sinit, int kg, int r0, in
 // exp2 and of the product dS = p * dp trail by one MFMA each (at D = 64 two
 // elements per MFMA).  P and dS go to `pds` as bf16 B fragments (P of the
 // lane's rows 0-7 / 8-15, then dS) as soon as 8 of them are done.  `mid()` runs
-// halfway through the stream (it loads the next step's starting values).
-template <int D, typename Mid>
+// halfway through the stream (it loads the next step's starting values);
+// `side(k)`, k < NSIDE, runs after MFMA k+1, early in the stream, so that the
+// tile loads it issues have most of two iterations to land.
+template <int D, int NSIDE, typename Mid, typename Side>
 __device__ __forceinline__ void dkdv_producer_iter(f32x16 &sa, f32x16 &dpa, const f32x16 &sb, const f32x16 &dpb,
-                                                   const bf16x8 *kf, const bf16x8 *vf, bf16x8 (&ring)[kKvAhead],
-                                                   uint32_t qst, const uint32_t *oq, const uint32_t *od,
-                                                   uint32_t pds, float c, Mid &&mid) {
+                                                   f32x16 &sn, const bf16x8 *kf, const bf16x8 *vf,
+                                                   bf16x8 (&ring)[kKvAhead], uint32_t qst, uint32_t qst_next,
+                                                   const uint32_t *oq, const uint32_t *od,
+                                                   uint32_t pds, float c, Mid &&mid, Side &&side) {
     constexpr int KK = D / 16, NSTEP = 2 * KK, EPB = 16 / NSTEP;
+    static_assert(NSIDE < NSTEP, "side work goes to distinct MFMA slots");
     static_assert(16 % NSTEP == 0, "softmax elements spread evenly over the MFMAs");
     float arg[16], pv[16], ds[16];
     auto write_half = [&](int hh) {
@@ -649,12 +661,20 @@ __device__ __forceinline__ void dkdv_producer_iter(f32x16 &sa, f32x16 &dpa, cons
 #pragma unroll
     for (int st = 0; st <= NSTEP; ++st) {
         if (st < NSTEP) {
+            // slot st: MFMA j = st + kEarly of step t, or S MFMA j - NSTEP of step t+1
             const bf16x8 a = ring[st % kKvAhead];
-            if (st + kKvAhead < NSTEP) ring[st % kKvAhead] = dkdv_sdp_frag<D>(st + kKvAhead, qst, oq, od);
-            if (st < KK)
-                sa = mfma32x32x16(a, kf[st], sa);
+            if (st + kKvAhead < NSTEP) {
+                const int f = st + kKvAhead + kEarly;
+                ring[st % kKvAhead] = f < NSTEP ? dkdv_sdp_frag<D>(f, qst, oq, od)
+                                                : dkdv_sdp_frag<D>(f - NSTEP, qst_next, oq, od);
+            }
+            const int j = st + kEarly;
+            if (j < KK)
+                sa = mfma32x32x16(a, kf[j], sa);
+            else if (j < NSTEP)
+                dpa = mfma32x32x16(a, vf[j - KK], dpa);
             else
-                dpa = mfma32x32x16(a, vf[st - KK], dpa);
+                sn = mfma32x32x16(a, kf[j - NSTEP], sn);
         }
 #pragma unroll
         for (int e = 0; e < EPB; ++e) {
@@ -664,6 +684,9 @@ __device__ __forceinline__ void dkdv_producer_iter(f32x16 &sa, f32x16 &dpa, cons
             if (r >= EPB) ds[r - EPB] = pv[r - EPB] * dpb[r - EPB];
         }
         if (st >= 1 && (st * EPB) % 8 == 0) write_half(st * EPB / 8 - 1);
+#pragma unroll
+        for (int k = 0; k < NSIDE; ++k)
+            if (k + 1 == st) side(k);
         if (st == KK) mid();
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -818,6 +841,68 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         }
     };
 
+    // Direct loads of a step into its LDS stage.  The Q and dO tiles are split
+    // evenly over the 4 waves of a role: the consumers load the first kAhead
+    // steps before the loop, and from then on the producers load step t+3 in
+    // iteration t, between their MFMAs.  Consumer 3 loads the 32 rows'
+    // -lse/scale (lanes 0-31) and -D (lanes 32-63, one statistics block
+    // later), one dword per lane in one instruction, kStatAhead steps ahead.
+    // Rows past N re-read row N-1 (masked by the producers); past the last
+    // step the loads re-read it into a free stage.
+    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvPairs;
+    static_assert(2 * Tile::INSTR % kKvPairs == 0 && Tile::INSTR % kDmaPerWave == 0,
+                  "Q and dO tiles split evenly over the waves of a role");
+    const bool loads_do = pair * kDmaPerWave >= Tile::INSTR;
+    const int u0 = (pair * kDmaPerWave) % Tile::INSTR;
+    const uint16_t *tens = loads_do ? p.dout : p.q;
+    const int64_t t_rs = loads_do ? p.do_rs : p.q_rs;
+    const int tile_lds = loads_do ? T::kDoBase : 0;
+    const uint32_t row_bytes = (uint32_t)t_rs * 2;
+    uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+        dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
+        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
+    }
+    // The cursor of a step to load, with its row pointers: at the group's
+    // first head (tb / sb) and at the step's head (tr / sr), so that no load
+    // multiplies by the head index.  The -D half's offset, hs * 4 bytes, fits
+    // the 32-bit lane offset: the launcher rejects statistics strides of 2^30.
+    struct LoadCur {
+        Cur cu;
+        const uint16_t *tb, *tr;
+        const float *sb, *sr;
+    };
+    const int64_t head_stride_st = 2 * sq.hs;
+    const uint32_t stat_off = lane < kQT ? 0u : (uint32_t)sq.hs * 4u;
+    const int64_t trow_step = (int64_t)kQT * t_rs;
+    const uint16_t *tb0 = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)(g * grp + h0) * D;
+    const float *sb0 = p.stats + sq.st0 + (int64_t)(g * grp + h0) * head_stride_st + first.r0;
+    const LoadCur load_first{first, tb0, tb0, sb0, sb0};
+    auto advance_load = [&](LoadCur &l) {
+        const int r0 = l.cu.r0, hi = l.cu.hi;
+        advance(l.cu);
+        if (l.cu.r0 != r0) {
+            l.tb -= trow_step;
+            l.sb -= kQT;
+            l.tr = l.tb;
+            l.sr = l.sb;
+        } else if (l.cu.hi != hi) {
+            l.tr += D;
+            l.sr += head_stride_st;
+        }
+    };
+    // load k of this wave's share of the step's Q or dO tile into stage st
+    auto tile_k = [&](const LoadCur &l, int st, int k) {
+        const int lim = min(N - 1 - l.cu.r0, kQT);  // last valid row within the tile
+        dma_b128_m0(l.tr, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
+                    lbase + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
+    };
+    auto stat_load = [&](const LoadCur &l, int st) {
+        const int r = min(lane & (kQT - 1), min(N - 1 - l.cu.r0, kQT));
+        dma_b32_m0(l.sr, (uint32_t)r * 4 + stat_off, lbase + T::kStatBase + T::stat_stage(st));
+    };
+
     if (producer) {
         const int key = kb0 + pair * kKeysPerWave + m;  // this lane's key (C column)
         // K and V rows of the producer's 32 keys as B fragments (column = key, k = head dim)
@@ -879,6 +964,9 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             }
         };
 
+        LoadCur lc = load_first;  // the consumers loaded steps 0 .. kAhead-1
+#pragma unroll
+        for (int i = 0; i < T::kAhead; ++i) advance_load(lc);
         fence_barrier();  // the consumers' first loads have landed
         // Three register sets rotate: step t accumulates in set t % 3, the
         // softmax of step t-1 reads set (t-1) % 3, and the starting values of
@@ -896,6 +984,11 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         bf16x8 ring[kKvAhead];
         dkdv_inits(s[0], dp[0], stat + T::stat_stage(0));
         prepare(s[0]);
+        // the early MFMAs come after the starting values are loaded (slot KK of the stream)
+        static_assert(kEarly < KK && kEarly + kKvAhead <= 2 * KK, "early MFMAs follow the loads");
+#pragma unroll
+        for (int j = 0; j < kEarly; ++j)  // step 0's first S MFMAs, as iteration -1 would have
+            s[0] = mfma32x32x16(dkdv_sdp_frag<D>(j, T::q_stage(0), oq, od), kf[j], s[0]);
         dkdv_sdp_prefetch<D>(ring, T::q_stage(0), oq, od);
         run([&](auto J) {
             constexpr int ST = decltype(J)::value;          // stage of step t
@@ -903,12 +996,20 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             constexpr int X = (ST + 1) % 3;                 // set of step t+1 (step t-2's, done)
             constexpr int NX = (ST + 1) % T::kStages;       // stage of step t+1
             constexpr int PB = (ST + 1) % 2;                // P/dS buffer of step t-1
-            // the starting values of step t+1 are loaded halfway through the stream
-            dkdv_producer_iter<D>(s[A], dp[A], s[Pv], dp[Pv], kf, vf, ring, T::q_stage(ST), oq, od,
-                                  pds + PB * T::kPds, c,
-                                  [&]() { dkdv_inits(s[X], dp[X], stat + T::stat_stage(NX)); });
-            next_step();
-            prepare(s[X]);
+            constexpr int NN = (ST + T::kAhead) % T::kStages;  // stage of step t+3
+            // the starting values of step t+1 are loaded (and masked) halfway
+            // through the stream, before its first S MFMAs at the end of it;
+            // the tile loads of step t+3 run between the MFMAs
+            dkdv_producer_iter<D, kDmaPerWave>(
+                s[A], dp[A], s[Pv], dp[Pv], s[X], kf, vf, ring, T::q_stage(ST), T::q_stage(NX), oq, od,
+                pds + PB * T::kPds, c,
+                [&]() {
+                    dkdv_inits(s[X], dp[X], stat + T::stat_stage(NX));
+                    next_step();
+                    prepare(s[X]);
+                },
+                [&](int k) { tile_k(lc, NN, k); });
+            advance_load(lc);
             dkdv_sdp_prefetch<D>(ring, T::q_stage(NX), oq, od);
             // P / dS of step t-1 stored before the barrier; the next step's
             // operand reads may stay in flight across it (they are waited for
@@ -917,99 +1018,40 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
             // write only LDS reads follow (16-byte reads of distinct addresses,
             // which the compiler cannot merge): the kKvAhead first fragments
             // of step t+1.  Waiting until at most that many are outstanding
-            // retires the writes.
-            __builtin_amdgcn_s_waitcnt(0xc07f | (kReadsAfterPds << 8));
+            // retires the writes.  The same wait lets only this iteration's
+            // tile loads stay in flight: step t+2's, which the producers read
+            // from the next iteration on, have landed.
+            static_assert(kDmaPerWave < 16, "vmcnt immediate");
+            __builtin_amdgcn_s_waitcnt(kDmaPerWave | 0x70 | (kReadsAfterPds << 8));
             fence_barrier();
         });
+        // no load may still be writing this workgroup's LDS when it exits
+        __builtin_amdgcn_s_waitcnt(0x70);
         return;
     }
 
     // ---- consumers: for keys 64 kh .. +64 and head dims 64 eh .. +64
     const int kh = pair >> 1, eh = pair & 1;
-    // Direct loads of a step into its LDS stage, issued between the
-    // consumers' MFMAs: the Q and dO tiles are split evenly over the 4
-    // consumers (each one's share inside one of the two); the last consumer
-    // also fetches the 32 rows' -lse/scale and -D, one dword per lane.  Rows
-    // past N re-read row N-1 (masked by the producers).
-    constexpr int kDmaPerWave = 2 * Tile::INSTR / kKvPairs;
-    static_assert(2 * Tile::INSTR % kKvPairs == 0 && Tile::INSTR % kDmaPerWave == 0,
-                  "Q and dO tiles split evenly over the consumers");
-    const bool loads_do = pair * kDmaPerWave >= Tile::INSTR;
-    const int u0 = (pair * kDmaPerWave) % Tile::INSTR;
-    const uint16_t *tens = loads_do ? p.dout : p.q;
-    const int64_t t_rs = loads_do ? p.do_rs : p.q_rs;
-    const int tile_lds = loads_do ? T::kDoBase : 0;
-    const uint32_t row_bytes = (uint32_t)t_rs * 2;
-    uint32_t dma_roff[kDmaPerWave], dma_gran[kDmaPerWave];
-#pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {
-        dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
-        dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
-    }
+    // Statistics run kStatAhead = 5 steps ahead: step t+5's go to the stage of
+    // step t-1, whose statistics the producers read in iteration t-2.  Before
+    // the barrier ending iteration t, step t+2's must have landed (the
+    // producers read them in iteration t+1): all but the 3 newest loads.
+    constexpr int kStatAhead = T::kStages - 1;
     const bool stats_wave = pair == kKvPairs - 1;
-    // The loads of a step, issued together: this consumer's share of the Q or
-    // dO tile of step `cu` into stage st, and on the last consumer the 32
-    // rows' -lse/scale (lanes 0-31) and -D (lanes 32-63, one statistics block
-    // later), one dword per lane in one instruction.  `trow` / `srow` point at
-    // the step's first row of the step's head.  Rows past N re-read row N-1
-    // (masked by the producers).  The -D half's offset, hs * 4 bytes, fits the
-    // 32-bit lane offset: the launcher rejects statistics strides of 2^30.
-    const int64_t head_stride_st = 2 * sq.hs;
-    const uint32_t stat_off = lane < kQT ? 0u : (uint32_t)sq.hs * 4u;
-    // load k of the step (k = kDmaPerWave: the statistics, last consumer only)
-    auto issue_k = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st, int k) {
-        const int lim = min(N - 1 - cu.r0, kQT);  // last valid row within the tile
-        if (k < kDmaPerWave) {
-            dma_b128_m0(trow, min(dma_roff[k], (uint32_t)lim * row_bytes) + dma_gran[k],
-                        lbase + tile_lds + T::q_stage(st) + (u0 + k) * 1024);
-        } else if (stats_wave) {
-            const int r = min(lane & (kQT - 1), lim);
-            dma_b32_m0(srow, (uint32_t)r * 4 + stat_off, lbase + T::kStatBase + T::stat_stage(st));
-        }
-    };
-    auto issue = [&](const Cur &cu, const uint16_t *trow, const float *srow, int st) {
-#pragma unroll
-        for (int k = 0; k <= kDmaPerWave; ++k) issue_k(cu, trow, srow, st, k);
-    };
-    // Loads run kAhead = 3 iterations ahead (past the last step they re-read
-    // it into a free stage), so every consumer has the same number in flight
-    // at each wait.  Iteration t issues step t+3; before the barrier ending
-    // it, step t+2 must have landed (the producer reads its statistics and
-    // first fragments in iteration t+1): all but this iteration's loads.
-    // A stage is rewritten three iterations after the consumers' last read
-    // of it (step t-3's stage takes step t+3; step t-3 was consumed in
-    // iteration t-1, whose reads its MFMAs waited for).
-    auto wait_next = [&]() {  // this iteration's loads: kDmaPerWave, and the statistics on the last consumer
-        if (stats_wave)
-            wait_vm_only<kDmaPerWave + 1>();
-        else
-            wait_vm_only<kDmaPerWave>();
-    };
-    // The cursor of the step to load next, with its row pointers: at the
-    // group's first head (trb / srb) and at the step's head (trow / srow), so
-    // that no load multiplies by the head index.
-    const uint16_t *trb = tens + (sq.tok0 + first.r0) * t_rs + (int64_t)(g * grp + h0) * D;
-    const float *srb = p.stats + sq.st0 + (int64_t)(g * grp + h0) * head_stride_st + first.r0;
-    const int64_t trow_step = (int64_t)kQT * t_rs;
-    const uint16_t *trow = trb;
-    const float *srow = srb;
-    auto advance_load = [&](Cur &cu) {
-        const int r0 = cu.r0, hi = cu.hi;
-        advance(cu);
-        if (cu.r0 != r0) {
-            trb -= trow_step;
-            srb -= kQT;
-            trow = trb;
-            srow = srb;
-        } else if (cu.hi != hi) {
-            trow += D;
-            srow += head_stride_st;
-        }
-    };
-    Cur iss = first;
+    LoadCur lt = load_first, ls = load_first;
     [&]<int... J>(std::integer_sequence<int, J...>) {
-        ((issue(iss, trow, srow, J), advance_load(iss)), ...);
+        (([&] {
+#pragma unroll
+             for (int k = 0; k < kDmaPerWave; ++k) tile_k(lt, J, k);
+             advance_load(lt);
+         }()),
+         ...);
     }(std::make_integer_sequence<int, T::kAhead>{});
+    if (stats_wave) {
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            ((stat_load(ls, J), advance_load(ls)), ...);
+        }(std::make_integer_sequence<int, kStatAhead>{});
+    }
     wait_vm<0>();  // the first steps have landed
     fence_barrier();
 
@@ -1046,7 +1088,7 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         constexpr int ST = decltype(J)::value;
         constexpr int PV = (ST + T::kStages - 2) % T::kStages;  // stage of step t-2
         constexpr int NX = (ST + T::kStages - 1) % T::kStages;  // stage of step t-1
-        constexpr int NN = (ST + T::kAhead) % T::kStages;       // stage of step t+3
+        constexpr int NS = (ST + kStatAhead) % T::kStages;      // statistics stage of step t+5
         const uint32_t buf = pds + (ST % 2) * T::kPds;          // P/dS of step t-2
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
@@ -1055,11 +1097,12 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
                 pb[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + ks * 64 * 16);
                 db[k2][ks] = lds_frag_at(buf + k2 * T::kPdsPair + (2 + ks) * 64 * 16);
             }
-        cons.template run<kDmaPerWave + 1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV),
-                                           [&](int k) { issue_k(iss, trow, srow, NN, k); });
-        advance_load(iss);
+        cons.template run<1>(dvacc, dkacc, pb, db, ring, T::q_stage(PV), [&](int) {
+            if (stats_wave) stat_load(ls, NS);
+        });
+        if (stats_wave) advance_load(ls);
         cons.prefetch(ring, T::q_stage(NX));
-        wait_next();
+        if (stats_wave) wait_vm_only<kStatAhead - 2>();
         fence_barrier();
     });
     // no load may still be writing this workgroup's LDS when it exits
