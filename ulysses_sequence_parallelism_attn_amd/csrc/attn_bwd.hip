@@ -170,15 +170,13 @@ struct DqOffs {
 // With DQ the first kQAhead<D> fragments are already in `ring` (dq_prefetch).
 // dP^T starts from `nd` (-D of the lane's query row in every register), so the
 // stream leaves dP^T - D in `dp`.
-// `side(k)`, k < NSIDE, runs between MFMAs spread over the stream.
-template <int D, bool DQ, bool SDP, int NSIDE, typename Side>
+template <int D, bool DQ, bool SDP>
 __device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f32x16 &s, f32x16 &dp, const f32x16 &nd,
                                         const bf16x8 *qf, const bf16x8 *dof, bf16x8 (&ring)[kQAhead<D>],
-                                        uint32_t pstage, uint32_t cstage, const DqOffs<D> &o, Side &&side) {
+                                        uint32_t pstage, uint32_t cstage, const DqOffs<D> &o) {
     constexpr int EB = D / 32, KK = D / 16;
     constexpr int NDQ = DQ ? 2 * EB : 0, NSD = SDP ? 2 * KK : 0, NSTEP = NDQ + NSD;
     static_assert(!DQ || NDQ >= kQAhead<D>, "the prefetched ring holds dQ steps only");
-    constexpr int EVERY = NSIDE > 0 ? NSTEP / NSIDE : 1;
     auto frag = [&](int st) -> bf16x8 {
         if (st < NDQ) {
             const uint32_t at = pstage + (st / EB) * 16 * D * 2;
@@ -210,8 +208,6 @@ __device__ __forceinline__ void dq_gemm(f32x16 *dqacc, const bf16x8 (&dsf)[2], f
             else
                 dp = mfma32x32x16(a, dof[kk], dp);
         }
-        if constexpr (NSIDE > 0)
-            if (st % EVERY == 1 && st / EVERY < NSIDE) side(st / EVERY);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -348,10 +344,11 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         dma_roff[k] = (uint32_t)Tile::row(u0 + k, lane) * row_bytes;
         dma_gran[k] = Tile::gran_bytes(u0 + k, lane);
     }
-    // The tile the next loads fetch, set up by dma_prep one body ahead (at
-    // the end of the dS half, off the MFMA stream): the address of its first
-    // key row (wave-uniform) and the byte offset of its last row inside N, so
-    // that a load in the MFMA stream is a clamp, an add and the M0 write.
+    // The tile the next loads fetch, set up by dma_prep one body ahead: the
+    // address of its first key row (wave-uniform) and the byte offset of its
+    // last row inside N, so that a load is a clamp, an add and the M0 write.
+    // The loads run at the end of the dS half, off the MFMA stream: issued
+    // between the MFMAs they made the MFMA half 2.8 % longer at N = 65536.
     const uint32_t dma_lds = (uint32_t)(uintptr_t)lds + tile_lds + u0 * 1024;
     const uint16_t *dma_tb = tens;
     uint32_t dma_lim = 0;
@@ -371,10 +368,11 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     auto visible = [&](int t) { return !p.causal || t * kDqKT <= i0 + kRowsPerWave - 1; };
 
     // The forward's schedule with a deeper ring: waves 4-7 run one barrier
-    // behind waves 0-3; tile t sits in stage t % 8 from its load (in the MFMA
+    // behind waves 0-3; tile t sits in stage t % 8 from its load (in the dS
     // half of tile t-6) to the lagging group's dQ of it (MFMA half of tile
     // t+1); each wave waits for its share of tile t+1 before the barrier
-    // ending its MFMA half of tile t (all but the 5 newest tiles' loads).
+    // ending its MFMA half of tile t (all but the 4 newest tiles' loads: its
+    // own loads of this body come after that wait).
     const bool lagging = wave >= kQWaves / 2;
     // The Q/dO/statistics loads above stay in flight while the first tiles'
     // loads are issued: loads retire in order, so the wait for tile 0 retires
@@ -405,22 +403,17 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
         // wave of its SIMD (busy with its dS) until its half ends.
         __builtin_amdgcn_s_setprio(2);
         if constexpr (FULL) {
-            dq_gemm<D, true, true, kDmaPerWave>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), stage(t), fo,
-                                                [&](int k) {
-                                                    if (more) issue_k(k, stage_next);
-                                                });
+            dq_gemm<D, true, true>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), stage(t), fo);
         } else {
-            if (more) issue(stage_next);
-            auto none = [](int) {};
             if (t >= 1 && visible(t - 1))
-                dq_gemm<D, true, false, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), 0, fo, none);
+                dq_gemm<D, true, false>(dqacc, dsf, s, dp, nd, qf, dof, ring, stage(t - 1), 0, fo);
             if (t < ntiles && visible(t))
-                dq_gemm<D, false, true, 0>(dqacc, dsf, s, dp, nd, qf, dof, ring, 0, stage(t), fo, none);
+                dq_gemm<D, false, true>(dqacc, dsf, s, dp, nd, qf, dof, ring, 0, stage(t), fo);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
         if (more)
-            wait_vm_barrier<(T::kAhead - 1) * kDmaPerWave>();
+            wait_vm_barrier<(T::kAhead - 2) * kDmaPerWave>();
         else
             wait_vm_barrier<0>();
         __builtin_amdgcn_sched_barrier(0);
@@ -431,6 +424,7 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
                 dq_ds<true>(dsf, s, dp, cn, kg, t * kDqKT, row, N, p.causal, c);
             dq_prefetch<D>(ring, stage(t), fo);
         }
+        if (more) issue(stage_next);
         dma_prep(t + T::kAhead + 1);  // the tile the next body loads
         fence_barrier();
     };
