@@ -813,8 +813,8 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
     // Iterations t = 0 .. nsteps+1, unrolled by the stage count so that every
     // stage offset and buffer parity is a constant: step t's tiles and
     // statistics sit in stage t % 6, its P/dS in buffer t % 2.  Past the last
-    // step the producer works on re-reads of the last step's tiles with every
-    // element masked, and what it stores is never read.
+    // step the producer works on re-reads of the last step's tiles, and what
+    // it computes from them is dropped or stored where no consumer reads.
     const int niter = nsteps + 2;
     // Whole groups in a straight loop, then the rest in a loop whose
     // iterations each test the count (a test per iteration inside the main
@@ -933,25 +933,18 @@ __device__ __forceinline__ void dkdv_body(const DkvParams &p, const int item) {
         const float c = p.scale_log2;
 
         // A step is masked when its rows reach below mlo (the causal diagonal)
-        // or above mhi (the ragged end), when the key block runs past N, and
-        // for every step past the last one (`left` counts the steps still to
-        // be prepared).  The producer needs only each step's first row: it
-        // drops by a tile every grp steps.
+        // or above mhi (the ragged end), or when the key block runs past N.
+        // The producer needs only each step's first row: it drops by a tile
+        // every grp steps.  The two steps past the last one need no mask:
+        // their S and dP are dropped, and the P / dS stored from the first of
+        // them goes to a buffer that no consumer reads again.
         const int mlo = kb0 + kKeysPerWg > N ? INT_MAX : (p.causal ? kb0 + kKeysPerWg : INT_MIN);
         const int mhi = N - kQT;
-        int r0 = first.r0, hc = gsteps, left = nsteps;
-        auto prepare = [&](f32x16 &sinit) {  // mask the S starting values of the step at (r0, left)
-            if (left <= 0 || r0 < mlo || r0 > mhi) {
-                if (left <= 0) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) sinit[r] = -INFINITY;
-                } else {
-                    dkdv_mask_init(sinit, kg, r0, key, N, p.causal);
-                }
-            }
+        int r0 = first.r0, hc = gsteps;
+        auto prepare = [&](f32x16 &sinit) {  // mask the S starting values of the step at r0
+            if (r0 < mlo || r0 > mhi) dkdv_mask_init(sinit, kg, r0, key, N, p.causal);
         };
         auto next_step = [&]() {
-            --left;
             if (--hc == 0) {
                 hc = gsteps;
                 r0 -= kQT;
