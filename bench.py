@@ -49,10 +49,34 @@ TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
 KERNEL_SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "relayout.hip", "mfma_tile.h", "ul_internal.h"]
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (string and character literals kept
+    as written), so that a comment edit does not count as a kernel change."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(ln.rstrip() for ln in "".join(out).splitlines() if ln.strip())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for n in KERNEL_SOURCES:
-        h.update((ROOT / "ulysses_sequence_parallelism_attn_amd" / "csrc" / n).read_bytes())
+        h.update(_code_only((ROOT / "ulysses_sequence_parallelism_attn_amd" / "csrc" / n).read_text()).encode())
     return h.hexdigest()[:16]
 
 

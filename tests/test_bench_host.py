@@ -75,3 +75,11 @@ def test_committed_traffic_matches_the_kernel_sources():
     rec = json.loads(bench.TRAFFIC_FILE.read_text())
     assert rec["kernel_hash"] == bench.kernel_hash(), "profiles/traffic.json is stale: re-run the counter passes"
     assert rec["workload"] == synth.WORKLOADS[3].name
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    src = 'int a = 1; // note\n/* block\n comment */ const char *s = "// kept"; char q = \'/\';\n\n  int b;'
+    same = '// header\nint a = 1;\n const char *s = "// kept"; char q = \'/\';\nint b;   /* tail */'
+    assert bench._code_only(src).split() == bench._code_only(same).split()
+    assert bench._code_only(src) != bench._code_only(src.replace('"// kept"', '"// changed"'))
+    assert bench._code_only(src) != bench._code_only(src.replace("int b;", "int c;"))

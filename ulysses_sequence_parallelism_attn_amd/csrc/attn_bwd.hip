@@ -501,10 +501,12 @@ __global__ __launch_bounds__(kQThreads) void attn_bwd_dq_bf16_kernel(DqParams p)
 // wave with MFMAs to issue:
 //   * the producer issues the 16 MFMAs of step t (S and dP) and, one element
 //     per MFMA, the softmax of step t-1 (whose S and dP it kept in a second
-//     accumulator set), storing P / dS of step t-1;
+//     accumulator set), storing P / dS of step t-1; it also issues the Q/dO
+//     tile loads of step t+3 and, before the barrier, the first S MFMAs of
+//     step t+1;
 //   * the consumer issues the 16 MFMAs of step t-2 on the P / dS that the
-//     producer stored in the previous iteration, and the tile loads of step
-//     t+3.
+//     producer stored in the previous iteration (and one consumer loads the
+//     rows' statistics a few steps ahead).
 // The producer needs no statistics registers and no mask branch in its
 // softmax: the S accumulator of a step starts from -lse/scale of its row
 // (or -inf where the key is masked: past the row, past N), the dP
