@@ -347,8 +347,9 @@ __device__ __forceinline__ void dq_body(const DqParams &p, const int item) {
     // The tile the next loads fetch, set up by dma_prep one body ahead: the
     // address of its first key row (wave-uniform) and the byte offset of its
     // last row inside N, so that a load is a clamp, an add and the M0 write.
-    // The loads run at the end of the dS half, off the MFMA stream: issued
-    // between the MFMAs they made the MFMA half 2.8 % longer at N = 65536.
+    // The loads run at the end of the dS half, off the MFMA stream (the dS
+    // half is the shorter one): issued between the MFMAs they cost the
+    // kernel 2.8 % of its time at N = 65536.
     const uint32_t dma_lds = (uint32_t)(uintptr_t)lds + tile_lds + u0 * 1024;
     const uint16_t *dma_tb = tens;
     uint32_t dma_lim = 0;
